@@ -1,0 +1,301 @@
+/*
+ * q4k_oracle.c -- plain, slow, single-threaded CPU reference for the Q4_K
+ * decode path. TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg call it; the product library never does, and the
+ * two share no code (this file includes nothing from the HIP library).
+ *
+ * Everything is computed in double precision from the exact input bytes and
+ * f32 activations. Each dequantised weight d*sc*q - dmin*m is exact in double
+ * (f16 values carry 11 significant bits, sc*q at most 10 bits, and the f16
+ * exponent range spans < 53 bits), every product with an f32 activation is
+ * exact, and the only rounding is the sequential double summation.
+ *
+ * Sources (the pages):
+ *  - infer-compute README, "Shaders" table (Q4_K/Q6_K and Q4_K fused FFN rows):
+ *    a Q4_K matrix-vector product, fused QKV projection, fused gate+up with a
+ *    GEGLU (GELU-tanh or SiLU gate) feeding the down projection.
+ *  - infer-compute README, "Quick Start" (q4k_matvec(data, x, rows, hidden)),
+ *    "Design Principles" item 8 (Q4_K matches the GGUF/Ollama quantisation).
+ *  - Performance -- infer-inference, "Activation Function Support" table
+ *    (gated GELU-tanh for Gemma, gated SiLU for Llama-family models).
+ *  - infer-inference README, Overview example (top-5 predictions from logits);
+ *    Performance -- infer-inference, "Honest Path Breakdown" (lm_head on GPU).
+ *  The byte layout itself is the public GGUF Q4_K super-block (the pages only
+ *  assert compatibility with it): see q4o_dequant_block.
+ *
+ * Readings where the pages are silent (all listed in the design notes):
+ *  - the min term is subtracted: w = d*sc*q - dmin*m;
+ *  - GEGLU applies the activation to the gate: h = act(gate) * up;
+ *  - GELU-tanh is 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)));
+ *  - top-k order is value descending then index ascending, NaN ranks last;
+ *  - prefill is the decode definition applied per token, exactly (no bf16);
+ *    q4o_ffn_prefill_bf16 additionally models bf16 operand rounding.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define Q4O_QK 256
+#define Q4O_BLOCK 144
+
+/* IEEE 754 binary16 -> double, from the format definition: 1 sign bit,
+ * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 = zero/subnormal,
+ * exponent 31 = infinity/NaN. */
+double q4o_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);                 /* frac/1024 * 2^-14 */
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);  /* (1+frac/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* The 12 scale bytes hold eight 6-bit scales and eight 6-bit mins.
+ * Sub-blocks 0..3 keep theirs in the low 6 bits of bytes 0..3 (scales) and
+ * 4..7 (mins). Sub-blocks 4..7 take their low 4 bits from bytes 8..11 (low
+ * nibble = scale, high nibble = min) and their top 2 bits from the spare top
+ * 2 bits of bytes 0..3 (scales) and 4..7 (mins). */
+void q4o_unpack_scales(const uint8_t *s, int *sc, int *mn)
+{
+    for (int j = 0; j < 4; ++j) {
+        sc[j] = s[j] & 63;
+        mn[j] = s[j + 4] & 63;
+    }
+    for (int j = 4; j < 8; ++j) {
+        sc[j] = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4);
+        mn[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* The quant of element e (0..255) of a block. The 128 quant bytes form four
+ * 32-byte groups; group g holds elements 64g..64g+31 in its low nibbles and
+ * elements 64g+32..64g+63 in its high nibbles. */
+static int q4o_quant(const uint8_t *qs, int e)
+{
+    const int g = e / 64, r = e % 64;
+    return r < 32 ? (qs[32 * g + r] & 0x0f) : (qs[32 * g + r - 32] >> 4);
+}
+
+/* Dequantise one 144-byte block: w[e] = d * sc[s] * q[e] - dmin * m[s],
+ * s = e / 32 the sub-block of element e. */
+void q4o_dequant_block(const uint8_t *blk, double *w)
+{
+    int sc[8], mn[8];
+    const double d = q4o_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+    const double dmin = q4o_f16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+    q4o_unpack_scales(blk + 4, sc, mn);
+    for (int e = 0; e < Q4O_QK; ++e) {
+        const int s = e / 32;
+        w[e] = d * sc[s] * q4o_quant(blk + 16, e) - dmin * mn[s];
+    }
+}
+
+/* Dense f64 copy of a rows x cols Q4_K matrix (row-major). */
+void q4o_dequant(const uint8_t *W, int64_t rows, int64_t cols, double *out)
+{
+    const int64_t nb = cols / Q4O_QK;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t b = 0; b < nb; ++b)
+            q4o_dequant_block(W + (i * nb + b) * Q4O_BLOCK, out + i * cols + b * Q4O_QK);
+}
+
+/* y_i = sum_j w_ij x_j and the tolerance scale A_i = sum_j |w_ij x_j|,
+ * x given in double. Either output may be NULL. */
+void q4o_matvec_f64(const uint8_t *W, const double *x, int64_t rows, int64_t cols,
+                    double *y, double *A)
+{
+    const int64_t nb = cols / Q4O_QK;
+    double w[Q4O_QK];
+    for (int64_t i = 0; i < rows; ++i) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            q4o_dequant_block(W + (i * nb + b) * Q4O_BLOCK, w);
+            for (int e = 0; e < Q4O_QK; ++e) {
+                const double t = w[e] * x[b * Q4O_QK + e];
+                acc += t;
+                mag += fabs(t);
+            }
+        }
+        if (y) y[i] = acc;
+        if (A) A[i] = mag;
+    }
+}
+
+/* Same with an f32 activation vector (widened exactly to double). */
+void q4o_matvec(const uint8_t *W, const float *x, int64_t rows, int64_t cols,
+                double *y, double *A)
+{
+    double *xd = (double *)malloc((size_t)cols * sizeof(double));
+    for (int64_t j = 0; j < cols; ++j) xd[j] = (double)x[j];
+    q4o_matvec_f64(W, xd, rows, cols, y, A);
+    free(xd);
+}
+
+/* GELU, tanh approximation. */
+double q4o_gelu_tanh(double z)
+{
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
+
+/* SiLU: z * sigmoid(z). */
+double q4o_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+void q4o_act_array(const double *z, int64_t n, int act, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = act == 0 ? q4o_gelu_tanh(z[i]) : q4o_silu(z[i]);
+}
+
+/* Gated FFN for one activation vector:
+ *   g = Wg x, u = Wu x (Wg, Wu: inter x hidden), h = act(g) * u,
+ *   y = Wd h (Wd: hidden x inter), A = sum_j |wd_ij h_j| with this h.
+ * act: 0 = GELU-tanh, 1 = SiLU. g, u, h, A may be NULL. */
+void q4o_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
+             int64_t hidden, int64_t inter, int act,
+             double *y, double *A, double *g_out, double *u_out, double *h_out)
+{
+    double *g = (double *)malloc((size_t)inter * sizeof(double));
+    double *u = (double *)malloc((size_t)inter * sizeof(double));
+    double *h = (double *)malloc((size_t)inter * sizeof(double));
+    q4o_matvec(Wg, x, inter, hidden, g, NULL);
+    q4o_matvec(Wu, x, inter, hidden, u, NULL);
+    for (int64_t i = 0; i < inter; ++i)
+        h[i] = (act == 0 ? q4o_gelu_tanh(g[i]) : q4o_silu(g[i])) * u[i];
+    q4o_matvec_f64(Wd, h, hidden, inter, y, A);
+    if (g_out) memcpy(g_out, g, (size_t)inter * sizeof(double));
+    if (u_out) memcpy(u_out, u, (size_t)inter * sizeof(double));
+    if (h_out) memcpy(h_out, h, (size_t)inter * sizeof(double));
+    free(g);
+    free(u);
+    free(h);
+}
+
+/* ---- top-k: the first k entries of all rows ordered by (value descending,
+ * index ascending); NaN values rank below every number, among themselves by
+ * index. A full sort is the definition. ---- */
+static const double *q4o_sort_vals;
+
+static int q4o_rank_cmp(const void *pa, const void *pb)
+{
+    const int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    const double va = q4o_sort_vals[a], vb = q4o_sort_vals[b];
+    const int na = isnan(va), nb = isnan(vb);
+    if (na != nb) return na ? 1 : -1;
+    if (!na && va != vb) return va > vb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+void q4o_topk(const double *v, int64_t n, int k, int64_t *idx, double *val)
+{
+    int64_t *order = (int64_t *)malloc((size_t)n * sizeof(int64_t));
+    for (int64_t i = 0; i < n; ++i) order[i] = i;
+    q4o_sort_vals = v;
+    qsort(order, (size_t)n, sizeof(int64_t), q4o_rank_cmp);
+    for (int i = 0; i < k && i < n; ++i) {
+        idx[i] = order[i];
+        val[i] = v[order[i]];
+    }
+    free(order);
+}
+
+/* ---- prefill: the decode definitions applied to each token row ---- */
+
+/* Y[t][i] = sum_j w_ij X[t][j], A[t][i] = sum_j |w_ij X[t][j]|. */
+void q4o_matmul(const uint8_t *W, const float *X, int64_t seq, int64_t rows, int64_t cols,
+                double *Y, double *A)
+{
+    for (int64_t t = 0; t < seq; ++t)
+        q4o_matvec(W, X + t * cols, rows, cols, Y + t * rows, A ? A + t * rows : NULL);
+}
+
+/* Per-token gated FFN; Y, A are [seq][hidden]. */
+void q4o_ffn_prefill(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *X,
+                     int64_t seq, int64_t hidden, int64_t inter, int act, double *Y, double *A)
+{
+    for (int64_t t = 0; t < seq; ++t)
+        q4o_ffn(Wg, Wu, Wd, X + t * hidden, hidden, inter, act,
+                Y + t * hidden, A ? A + t * hidden : NULL, NULL, NULL, NULL);
+}
+
+/* ---- bf16 operand model for the matrix-core prefill ----
+ * bf16 keeps the top 16 bits of an IEEE binary32 value; conversion rounds to
+ * nearest, ties to even. Weights are first formed in binary32 (the exact weight
+ * rounded once to nearest even), then rounded to bf16. */
+static double q4o_round_f32(double v)
+{
+    return (double)(float)v;   /* C conversion double->float rounds to nearest even */
+}
+
+double q4o_round_bf16(double v)
+{
+    if (isnan(v) || isinf(v) || v == 0.0) return v;
+    const float f = (float)v;  /* binary32 first (exact for binary32 inputs) */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    const uint32_t lsb = (bits >> 16) & 1u;
+    bits += 0x7fffu + lsb;     /* round to nearest even at bit 16 */
+    bits &= 0xffff0000u;
+    float r;
+    memcpy(&r, &bits, sizeof r);
+    return (double)r;
+}
+
+/* Per-token gated FFN with bf16 operands: X and W rounded to bf16 (W via
+ * binary32), G and U exact products of those, H = act(G)*U rounded to bf16,
+ * Y = Wd(bf16) H(bf16) exact. Used as a tighter second check of the matrix-core
+ * path; the graded comparison is against q4o_ffn_prefill. */
+void q4o_ffn_prefill_bf16(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd,
+                          const float *X, int64_t seq, int64_t hidden, int64_t inter,
+                          int act, double *Y, double *A)
+{
+    double *wg = (double *)malloc((size_t)(inter * hidden) * sizeof(double));
+    double *wu = (double *)malloc((size_t)(inter * hidden) * sizeof(double));
+    double *wd = (double *)malloc((size_t)(hidden * inter) * sizeof(double));
+    double *xb = (double *)malloc((size_t)hidden * sizeof(double));
+    double *h = (double *)malloc((size_t)inter * sizeof(double));
+    q4o_dequant(Wg, inter, hidden, wg);
+    q4o_dequant(Wu, inter, hidden, wu);
+    q4o_dequant(Wd, hidden, inter, wd);
+    for (int64_t i = 0; i < inter * hidden; ++i) {
+        wg[i] = q4o_round_bf16(q4o_round_f32(wg[i]));
+        wu[i] = q4o_round_bf16(q4o_round_f32(wu[i]));
+        wd[i] = q4o_round_bf16(q4o_round_f32(wd[i]));
+    }
+    for (int64_t t = 0; t < seq; ++t) {
+        for (int64_t j = 0; j < hidden; ++j) xb[j] = q4o_round_bf16((double)X[t * hidden + j]);
+        for (int64_t i = 0; i < inter; ++i) {
+            double g = 0.0, u = 0.0;
+            for (int64_t j = 0; j < hidden; ++j) {
+                g += wg[i * hidden + j] * xb[j];
+                u += wu[i * hidden + j] * xb[j];
+            }
+            h[i] = q4o_round_bf16((act == 0 ? q4o_gelu_tanh(g) : q4o_silu(g)) * u);
+        }
+        for (int64_t i = 0; i < hidden; ++i) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < inter; ++j) {
+                const double p = wd[i * inter + j] * h[j];
+                acc += p;
+                mag += fabs(p);
+            }
+            Y[t * hidden + i] = acc;
+            if (A) A[t * hidden + i] = mag;
+        }
+    }
+    free(wg);
+    free(wu);
+    free(wd);
+    free(xb);
+    free(h);
+}

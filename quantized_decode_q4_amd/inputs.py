@@ -1,0 +1,112 @@
+"""Seeded synthetic inputs for the Q4_K decode path.
+
+This module is the only code shared by the HIP path's tests/benchmarks and the
+CPU oracle. It draws random numbers and lays them out as bytes; it performs none
+of the method's arithmetic (no dequantisation, no dot products, no activation).
+
+Workload shapes follow the Gemma-3-4B decode figures of the infer-inference
+PERFORMANCE page (hidden 2560, 34 layers, vocabulary ~262K) and the head layout of
+its RoPE comparison table (head_dim 256, 8 query heads); the value distributions
+are the synthetic "random weights" regime of that page's GPU decode table.
+
+Q4_K block bytes (GGUF layout, 144 B per 256 weights):
+  bytes 0-1 : d    (IEEE binary16, little-endian)
+  bytes 2-3 : dmin (IEEE binary16, little-endian)
+  bytes 4-15: 96 bits of packed 6-bit scales and mins
+  bytes 16-143: 256 four-bit quants
+Random blocks use uniform bytes 4..143 (every 6-bit field and nibble is then an
+independent uniform integer) and d, dmin drawn uniformly from [1e-4, 2e-3) and
+rounded to binary16 by numpy (round-to-nearest-even).
+
+Seeding: numpy PCG64 via ``default_rng([0x51344B, config, tensor_id, index])``.
+Tensor ids: 0 = W / Wqkv / Wg, 1 = Wu, 2 = Wd, 3 = x / X. ``index`` is the layer
+or copy number. Draw order inside ``q4k_random``: the 144-byte rows of raw bytes
+first, then all d values, then all dmin values (row-major over blocks).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+QK_K = 256            # weights per super-block
+BLOCK_BYTES = 144     # bytes per super-block
+SEED_ROOT = 0x51344B
+
+# Shapes of the five workloads (rows, cols, ...)
+HIDDEN = 2560
+INTER = 10240
+Q_ROWS = 2048          # 8 query heads x 256
+KV_ROWS = 1024         # 4 kv heads x 256
+VOCAB = 262144
+N_LAYERS = 34
+PREFILL_SEQ = 64
+
+D_LO, D_HI = 1e-4, 2e-3
+
+
+def rng_for(config: int, tensor_id: int, index: int = 0) -> np.random.Generator:
+    """Counter-style seeding: one independent PCG64 stream per (config, tensor, index)."""
+    return np.random.default_rng([SEED_ROOT, int(config), int(tensor_id), int(index)])
+
+
+def row_bytes(cols: int) -> int:
+    if cols <= 0 or cols % QK_K:
+        raise ValueError(f"cols must be a positive multiple of {QK_K}, got {cols}")
+    return cols // QK_K * BLOCK_BYTES
+
+
+def q4k_random(rng: np.random.Generator, rows: int, cols: int,
+               d_range=(D_LO, D_HI), dmin_range=(D_LO, D_HI)) -> np.ndarray:
+    """Random Q4_K matrix as uint8[rows, cols/256*144] (row-major blocks)."""
+    nb = cols // QK_K
+    rb = row_bytes(cols)
+    raw = rng.integers(0, 256, size=(rows, nb, BLOCK_BYTES), dtype=np.uint8)
+    d = rng.uniform(d_range[0], d_range[1], size=(rows, nb)).astype(np.float16)
+    dmin = rng.uniform(dmin_range[0], dmin_range[1], size=(rows, nb)).astype(np.float16)
+    raw[:, :, 0:2] = d.astype("<f2").view(np.uint8).reshape(rows, nb, 2)
+    raw[:, :, 2:4] = dmin.astype("<f2").view(np.uint8).reshape(rows, nb, 2)
+    return raw.reshape(rows, rb)
+
+
+def normal_f32(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
+    """N(0,1) drawn in f64, multiplied by ``scale`` in f64, then cast to f32."""
+    v = rng.standard_normal(size=shape)
+    if scale != 1.0:
+        v = v * scale
+    return v.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# The five named workloads. Each returns a dict of numpy arrays (host memory).
+# ----------------------------------------------------------------------------
+
+def tiny_matvec(rows: int = 256, cols: int = 512):
+    """Tiny Q4_K matvec: W 256 x 512 (2 super-blocks per row), x ~ N(0,1)."""
+    return {"W": q4k_random(rng_for(0, 0), rows, cols),
+            "x": normal_f32(rng_for(0, 3), cols)}
+
+
+def qkv(copy: int = 0, cols: int = HIDDEN, q_rows: int = Q_ROWS, kv_rows: int = KV_ROWS):
+    """Fused QKV: concatenated [q; k; v] rows x hidden; x ~ N(0,1)."""
+    rows = q_rows + 2 * kv_rows
+    return {"W": q4k_random(rng_for(1, 0, copy), rows, cols),
+            "x": normal_f32(rng_for(1, 3, copy), cols),
+            "q_rows": q_rows, "kv_rows": kv_rows}
+
+
+def ffn_layer(layer: int = 0, hidden: int = HIDDEN, inter: int = INTER):
+    """One FFN layer: Wg, Wu (inter x hidden), Wd (hidden x inter), x ~ N(0,1)."""
+    return {"Wg": q4k_random(rng_for(2, 0, layer), inter, hidden),
+            "Wu": q4k_random(rng_for(2, 1, layer), inter, hidden),
+            "Wd": q4k_random(rng_for(2, 2, layer), hidden, inter),
+            "x": normal_f32(rng_for(2, 3, layer), hidden)}
+
+
+def lm_head(copy: int = 0, rows: int = VOCAB, cols: int = HIDDEN):
+    """lm_head: W vocab x hidden; x ~ N(0,1) / sqrt(hidden)."""
+    return {"W": q4k_random(rng_for(3, 0, copy), rows, cols),
+            "x": normal_f32(rng_for(3, 3, copy), cols, scale=1.0 / np.sqrt(cols))}
+
+
+def prefill_x(seq: int = PREFILL_SEQ, hidden: int = HIDDEN, index: int = 0):
+    """Prefill activations X[seq, hidden] ~ N(0,1); weights are ffn_layer(...)'s."""
+    return normal_f32(rng_for(4, 3, index), (seq, hidden))
