@@ -1,0 +1,162 @@
+/*
+ * q4k.h -- C ABI of the MI355X (gfx950) Q4_K decode library (libq4k.so).
+ *
+ * The library computes the block-quantised matrix-vector products of
+ * transformer decode on Q4_K weights: a plain matvec, the fused QKV
+ * projection, the fused gate+up -> gated activation -> down FFN, the
+ * vocabulary-sized lm_head with top-k, and a small-batch prefill matmul.
+ *
+ * Sources (the pages):
+ *  - infer-compute README, "Shaders" table, rows "Q4_K/Q6_K" (q4k_matvec,
+ *    q4k_qkv_proj) and "Q4_K fused FFN" (gate+up fused with a shared input,
+ *    GELU-tanh / SiLU gated down projection); "Quick Start" (q4k_matvec takes
+ *    the quantised bytes, the activation, rows and hidden size; prefill for
+ *    seq > 1); "Key Optimizations" table (pre-allocated buffers, fused
+ *    gate+up); "Design Principles" item 8 (Q4_K matches the GGUF format).
+ *  - Performance -- infer-inference, "Activation Function Support" table
+ *    (gated GELU-tanh, gated SiLU); "Honest Path Breakdown" and "Real vindex"
+ *    table (lm_head on the GPU, top predictions).
+ *  - infer-inference README, Overview example (top-5 predictions).
+ *
+ * Q4_K weight layout (GGUF super-block, 144 bytes per 256 weights):
+ *   bytes 0-1  d     IEEE binary16, little-endian
+ *   bytes 2-3  dmin  IEEE binary16, little-endian
+ *   bytes 4-15 eight 6-bit scales sc[s] and eight 6-bit mins m[s]
+ *              (s < 4: low 6 bits of bytes 4+s and 8+s; s >= 4: nibbles of
+ *              byte 12+s-4 plus the top 2 bits of bytes 4+s-4 / 8+s-4)
+ *   bytes 16-143 quants: byte 16+32g+r holds element 64g+r (low nibble) and
+ *              element 64g+32+r (high nibble)
+ *   weight e = d * sc[e/32] * q[e] - dmin * m[e/32]
+ * A rows x cols matrix is rows * (cols/256) consecutive blocks, row-major; the
+ * row stride is cols/256*144 bytes. cols must be a positive multiple of 256.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or keeps device memory; intermediates go in the
+ *    caller's workspace `ws` (size from the matching *_workspace_bytes call).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on it and the call returns without synchronising; results are valid once
+ *    the stream has reached that point.
+ *  - Arguments are checked before anything is enqueued. On an argument error
+ *    the call returns a negative q4k_status, enqueues nothing and leaves every
+ *    output untouched. rows == 0 (or seq == 0) is a successful no-op.
+ *  - Checks: null pointers (for non-empty tensors); cols not a positive
+ *    multiple of 256 or above Q4K_COLS_MAX; negative sizes; W, x, X and
+ *    workspaces not 16-byte aligned; an output range overlapping an input
+ *    range or another output; unknown activation; workspace too small.
+ *  - A failed kernel launch returns Q4K_ERR_HIP; q4k_last_hip_error() then
+ *    returns the HIP error string (thread-local).
+ *  - Calls hold no global state (apart from a per-device cache of the compute
+ *    unit count) and are re-entrant; calls on one stream execute in order.
+ *  - Results are deterministic: no atomics, one writer per output element.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum q4k_status {
+    Q4K_OK = 0,
+    Q4K_ERR_NULL = -1,      /* a required pointer is NULL */
+    Q4K_ERR_SHAPE = -2,     /* bad rows / cols / seq / split sizes */
+    Q4K_ERR_ALIGN = -3,     /* W, x, X or a workspace not 16-byte aligned */
+    Q4K_ERR_K = -4,         /* top-k count outside 1..min(rows, Q4K_TOPK_MAX) */
+    Q4K_ERR_ACT = -5,       /* unknown activation */
+    Q4K_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required */
+    Q4K_ERR_ALIAS = -7,     /* an output overlaps an input or another output */
+    Q4K_ERR_HIP = -8        /* a HIP runtime/launch error */
+};
+
+enum q4k_act {
+    Q4K_ACT_GELU_TANH = 0,  /* 0.5 z (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3))) */
+    Q4K_ACT_SILU = 1        /* z / (1 + exp(-z)) */
+};
+
+#define Q4K_QK 256            /* weights per super-block */
+#define Q4K_BLOCK_BYTES 144   /* bytes per super-block */
+#define Q4K_TOPK_MAX 64       /* largest k of q4k_lmhead_topk */
+#define Q4K_COLS_MAX 65536    /* largest cols (reduction length) */
+
+/* y[i] = sum_j W[i][j] * x[j], i < rows.
+ * Source: infer-compute README, "Quick Start" (q4k_matvec) and "Shaders"
+ * table (q4k_matvec). W: rows x cols Q4_K; x: f32[cols]; y: f32[rows]. */
+int q4k_matvec(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
+               void *stream);
+
+/* Fused QKV projection: one pass over the concatenated rows [q; k; v] of Wqkv
+ * ((q_rows + 2*kv_rows) x cols), all sharing x; rows [0, q_rows) go to q,
+ * [q_rows, q_rows+kv_rows) to k, the rest to v.
+ * Source: infer-compute README, "Shaders" table (q4k_qkv_proj). */
+int q4k_qkv(const void *Wqkv, const float *x, float *q, float *k, float *v,
+            int64_t q_rows, int64_t kv_rows, int64_t cols, void *stream);
+
+/* First FFN stage: g = Wg x and u = Wu x computed in the same pass over x
+ * (Wg, Wu: inter x hidden), h[i] = act(g[i]) * u[i], h: f32[inter].
+ * Source: infer-compute README, "Shaders" table (q4k_ffn_gate_up, "fused
+ * gate+up, shared input") and "Activation" row (geglu_gelu_tanh/geglu_silu). */
+int q4k_gate_up(const void *Wg, const void *Wu, const float *x, float *h,
+                int64_t inter, int64_t hidden, int act, void *stream);
+
+/* Workspace of q4k_ffn: h, f32[inter] (16-byte aligned). */
+size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter);
+
+/* Gated FFN for one token: h = act(Wg x) * (Wu x) (q4k_gate_up), then
+ * y = Wd h (Wd: hidden x inter). x: f32[hidden]; y: f32[hidden]; h lives in
+ * ws. Source: infer-compute README, "Shaders" table (q4k_ffn_gate_up followed
+ * by q4k_geglu_gelu_tanh_down / q4k_geglu_silu_down). */
+int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
+            int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace of q4k_lmhead_topk: per-workgroup top-k candidates. */
+size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k);
+
+/* logits = W x over all rows (the vocabulary), then the k largest logits in
+ * order of value descending, index ascending (NaN logits rank last).
+ * top_idx: int32[k]; top_val: f32[k] (the logits at those rows). Requires
+ * 1 <= k <= min(rows, Q4K_TOPK_MAX).
+ * Source: Performance -- infer-inference, "Honest Path Breakdown" (GPU
+ * logits) and "Real vindex" table (lm_head); infer-inference README, Overview
+ * example (top-5 predictions). */
+int q4k_lmhead_topk(const void *W, const float *x, float *logits, int64_t rows, int64_t cols,
+                    int k, int32_t *top_idx, float *top_val, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Workspace of q4k_matmul (bf16 copy of X for seq >= 64; 0 otherwise). */
+size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq);
+
+/* Small-batch matmul for prefill: Y[t][i] = sum_j W[i][j] X[t][j],
+ * X: f32[seq][cols], Y: f32[seq][rows] (token-major). seq >= 64 runs on the
+ * matrix cores with bf16 operands (weights dequantised to bf16 tiles in LDS,
+ * fp32 accumulation); smaller seq runs the f32 matvec once per token.
+ * Source: infer-compute README, "Quick Start" (GPU prefill for seq > 1). */
+int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
+               int64_t seq, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace of q4k_ffn_prefill. */
+size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, int64_t inter);
+
+/* Gated FFN for seq tokens: H = act(X Wg^T) * (X Wu^T), Y = H Wd^T.
+ * X, Y: f32[seq][hidden]. seq >= 64: bf16 matrix-core path with the gated
+ * activation applied to fp32 G/U before H is rounded to bf16; smaller seq:
+ * q4k_ffn per token. Source: infer-compute README, "Quick Start" (prefill)
+ * and "Shaders" table (Q4_K fused FFN row). */
+int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, const float *X, float *Y,
+                    int64_t seq, int64_t hidden, int64_t inter, int act,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a q4k_status value (static string). */
+const char *q4k_status_string(int status);
+
+/* The HIP error string of the last Q4K_ERR_HIP on this thread ("" if none). */
+const char *q4k_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4K_H */

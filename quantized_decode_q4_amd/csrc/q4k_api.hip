@@ -1,0 +1,263 @@
+// C ABI of libq4k.so: argument checking, workspace carving and dispatch.
+// Every check runs before anything is enqueued, so a failing call leaves the
+// stream and all outputs untouched. Semantics of each call: include/q4k.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "q4k.h"
+#include "q4k_internal.h"
+
+#define Q4K_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return Q4K_OK;
+    snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return Q4K_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Half-open byte range of a tensor; empty ranges overlap nothing.
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span(const void *p, int64_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool cols_ok(int64_t cols) { return cols > 0 && cols % Q4K_QK == 0 && cols <= Q4K_COLS_MAX; }
+bool rows_ok(int64_t rows) { return rows >= 0 && rows <= INT32_MAX; }
+int64_t wbytes(int64_t rows, int64_t cols) { return rows * (cols / Q4K_QK) * Q4K_BLOCK_BYTES; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int64_t kMfmaMinSeq = 64;  // seq at which prefill switches to the matrix cores
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+Q4K_EXPORT const char *q4k_status_string(int status)
+{
+    switch (status) {
+        case Q4K_OK: return "Q4K_OK";
+        case Q4K_ERR_NULL: return "Q4K_ERR_NULL: a required pointer is NULL";
+        case Q4K_ERR_SHAPE: return "Q4K_ERR_SHAPE: invalid rows/cols/seq (cols must be a positive multiple of 256, <= 65536)";
+        case Q4K_ERR_ALIGN: return "Q4K_ERR_ALIGN: W, x, X and workspaces must be 16-byte aligned";
+        case Q4K_ERR_K: return "Q4K_ERR_K: k must satisfy 1 <= k <= min(rows, 64)";
+        case Q4K_ERR_ACT: return "Q4K_ERR_ACT: unknown activation";
+        case Q4K_ERR_WORKSPACE: return "Q4K_ERR_WORKSPACE: workspace NULL or too small";
+        case Q4K_ERR_ALIAS: return "Q4K_ERR_ALIAS: an output overlaps an input or another output";
+        case Q4K_ERR_HIP: return "Q4K_ERR_HIP: HIP runtime error (see q4k_last_hip_error)";
+        default: return "unknown q4k status";
+    }
+}
+
+Q4K_EXPORT const char *q4k_last_hip_error(void) { return g_last_hip_error; }
+
+Q4K_EXPORT int q4k_matvec(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
+                          void *stream)
+{
+    if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
+    if (rows == 0) return Q4K_OK;
+    if (!W || !x || !y) return Q4K_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_ERR_ALIGN;
+    const Span sy = span(y, rows * 4);
+    if (overlap(sy, span(W, wbytes(rows, cols))) || overlap(sy, span(x, cols * 4)))
+        return Q4K_ERR_ALIAS;
+    return hip_status(q4k::launch_rows_store((const uint8_t *)W, x, y, nullptr, nullptr, rows,
+                                             cols, rows, rows, as_stream(stream)));
+}
+
+Q4K_EXPORT int q4k_qkv(const void *Wqkv, const float *x, float *q, float *k, float *v,
+                       int64_t q_rows, int64_t kv_rows, int64_t cols, void *stream)
+{
+    if (q_rows < 0 || kv_rows < 0 || !cols_ok(cols)) return Q4K_ERR_SHAPE;
+    const int64_t rows = q_rows + 2 * kv_rows;
+    if (!rows_ok(rows)) return Q4K_ERR_SHAPE;
+    if (rows == 0) return Q4K_OK;
+    if (!Wqkv || !x || (q_rows && !q) || (kv_rows && (!k || !v))) return Q4K_ERR_NULL;
+    if (!aligned(Wqkv, 16) || !aligned(x, 16) || !aligned(q, 4) || !aligned(k, 4) ||
+        !aligned(v, 4))
+        return Q4K_ERR_ALIGN;
+    const Span in[2] = {span(Wqkv, wbytes(rows, cols)), span(x, cols * 4)};
+    const Span out[3] = {span(q, q_rows * 4), span(k, kv_rows * 4), span(v, kv_rows * 4)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlap(out[i], in[j])) return Q4K_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(out[i], out[j])) return Q4K_ERR_ALIAS;
+    }
+    return hip_status(q4k::launch_rows_store((const uint8_t *)Wqkv, x, q, k, v, rows, cols,
+                                             q_rows, q_rows + kv_rows, as_stream(stream)));
+}
+
+Q4K_EXPORT int q4k_gate_up(const void *Wg, const void *Wu, const float *x, float *h,
+                           int64_t inter, int64_t hidden, int act, void *stream)
+{
+    if (!rows_ok(inter) || !cols_ok(hidden)) return Q4K_ERR_SHAPE;
+    if (act != Q4K_ACT_GELU_TANH && act != Q4K_ACT_SILU) return Q4K_ERR_ACT;
+    if (inter == 0) return Q4K_OK;
+    if (!Wg || !Wu || !x || !h) return Q4K_ERR_NULL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(h, 4))
+        return Q4K_ERR_ALIGN;
+    const Span sh = span(h, inter * 4);
+    if (overlap(sh, span(Wg, wbytes(inter, hidden))) || overlap(sh, span(Wu, wbytes(inter, hidden))) ||
+        overlap(sh, span(x, hidden * 4)))
+        return Q4K_ERR_ALIAS;
+    return hip_status(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu, x, h, inter,
+                                          hidden, act, as_stream(stream)));
+}
+
+Q4K_EXPORT size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter)
+{
+    if (!cols_ok(hidden) || !cols_ok(inter)) return 0;
+    return round_up((size_t)inter * 4, 256);
+}
+
+Q4K_EXPORT int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
+                       int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    if (!cols_ok(hidden) || !cols_ok(inter)) return Q4K_ERR_SHAPE;
+    if (act != Q4K_ACT_GELU_TANH && act != Q4K_ACT_SILU) return Q4K_ERR_ACT;
+    if (!Wg || !Wu || !Wd || !x || !y) return Q4K_ERR_NULL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(x, 16) ||
+        !aligned(y, 4))
+        return Q4K_ERR_ALIGN;
+    const size_t need = q4k_ffn_workspace_bytes(hidden, inter);
+    if (!ws || ws_bytes < need) return Q4K_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return Q4K_ERR_ALIGN;
+    const Span in[4] = {span(Wg, wbytes(inter, hidden)), span(Wu, wbytes(inter, hidden)),
+                        span(Wd, wbytes(hidden, inter)), span(x, hidden * 4)};
+    const Span sy = span(y, hidden * 4), sw = span(ws, (int64_t)need);
+    if (overlap(sy, sw)) return Q4K_ERR_ALIAS;
+    for (int j = 0; j < 4; ++j)
+        if (overlap(sy, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
+    float *h = (float *)ws;
+    hipStream_t s = as_stream(stream);
+    int st = hip_status(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu, x, h, inter,
+                                            hidden, act, s));
+    if (st != Q4K_OK) return st;
+    return hip_status(
+        q4k::launch_rows_store((const uint8_t *)Wd, h, y, nullptr, nullptr, hidden, inter, hidden,
+                               hidden, s));
+}
+
+Q4K_EXPORT size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k)
+{
+    if (!rows_ok(rows) || !cols_ok(cols) || rows == 0 || k < 1 || k > Q4K_TOPK_MAX) return 0;
+    return round_up((size_t)q4k::lmhead_num_wgs(rows, cols) * (size_t)k * 8, 256);
+}
+
+Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int64_t rows,
+                               int64_t cols, int k, int32_t *top_idx, float *top_val, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
+    if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
+    const int64_t nwg = q4k::lmhead_num_wgs(rows, cols);
+    if (nwg * k > q4k::kMergeCandMax) return Q4K_ERR_SHAPE;
+    if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||
+        !aligned(top_val, 4))
+        return Q4K_ERR_ALIGN;
+    const size_t need = q4k_lmhead_workspace_bytes(rows, cols, k);
+    if (!ws || ws_bytes < need) return Q4K_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return Q4K_ERR_ALIGN;
+    const Span in[2] = {span(W, wbytes(rows, cols)), span(x, cols * 4)};
+    const Span out[4] = {span(logits, rows * 4), span(top_idx, (int64_t)k * 4),
+                         span(top_val, (int64_t)k * 4), span(ws, (int64_t)need)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlap(out[i], in[j])) return Q4K_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(out[i], out[j])) return Q4K_ERR_ALIAS;
+    }
+    return hip_status(q4k::launch_lmhead_topk((const uint8_t *)W, x, logits, rows, cols, k,
+                                              (uint64_t *)ws, top_idx, top_val, as_stream(stream)));
+}
+
+Q4K_EXPORT size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq)
+{
+    if (!rows_ok(rows) || !cols_ok(cols) || seq < 0) return 0;
+    if (seq < kMfmaMinSeq) return 0;
+    return round_up((size_t)seq * (size_t)cols * 2, 256);
+}
+
+Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
+                          int64_t seq, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!rows_ok(rows) || !cols_ok(cols) || seq < 0 || seq > INT32_MAX) return Q4K_ERR_SHAPE;
+    if (rows == 0 || seq == 0) return Q4K_OK;
+    if (!W || !X || !Y) return Q4K_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return Q4K_ERR_ALIGN;
+    const size_t need = q4k_matmul_workspace_bytes(rows, cols, seq);
+    if (need && (!ws || ws_bytes < need)) return Q4K_ERR_WORKSPACE;
+    if (need && !aligned(ws, 16)) return Q4K_ERR_ALIGN;
+    const Span sY = span(Y, seq * rows * 4), sw = span(ws, (int64_t)need);
+    const Span in[2] = {span(W, wbytes(rows, cols)), span(X, seq * cols * 4)};
+    if (overlap(sY, sw)) return Q4K_ERR_ALIAS;
+    for (int j = 0; j < 2; ++j)
+        if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
+    hipStream_t s = as_stream(stream);
+    // f32 path: one matvec per token (every token re-reads W).
+    for (int64_t t = 0; t < seq; ++t) {
+        const int st = hip_status(q4k::launch_rows_store((const uint8_t *)W, X + t * cols,
+                                                         Y + t * rows, nullptr, nullptr, rows,
+                                                         cols, rows, rows, s));
+        if (st != Q4K_OK) return st;
+    }
+    return Q4K_OK;
+}
+
+Q4K_EXPORT size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, int64_t inter)
+{
+    if (seq < 0 || !cols_ok(hidden) || !cols_ok(inter)) return 0;
+    size_t need = round_up((size_t)inter * 4, 256);
+    if (seq >= kMfmaMinSeq) {
+        const size_t mm = round_up((size_t)seq * (size_t)hidden * 2, 256) +
+                          round_up((size_t)seq * (size_t)inter * 2, 256);
+        need = mm > need ? mm : need;
+    }
+    return need;
+}
+
+Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, const float *X,
+                               float *Y, int64_t seq, int64_t hidden, int64_t inter, int act,
+                               void *ws, size_t ws_bytes, void *stream)
+{
+    if (seq < 0 || seq > INT32_MAX || !cols_ok(hidden) || !cols_ok(inter)) return Q4K_ERR_SHAPE;
+    if (act != Q4K_ACT_GELU_TANH && act != Q4K_ACT_SILU) return Q4K_ERR_ACT;
+    if (seq == 0) return Q4K_OK;
+    if (!Wg || !Wu || !Wd || !X || !Y) return Q4K_ERR_NULL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(X, 16) ||
+        !aligned(Y, 4))
+        return Q4K_ERR_ALIGN;
+    const size_t need = q4k_ffn_prefill_workspace_bytes(seq, hidden, inter);
+    if (!ws || ws_bytes < need) return Q4K_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return Q4K_ERR_ALIGN;
+    const Span in[4] = {span(Wg, wbytes(inter, hidden)), span(Wu, wbytes(inter, hidden)),
+                        span(Wd, wbytes(hidden, inter)), span(X, seq * hidden * 4)};
+    const Span sY = span(Y, seq * hidden * 4), sw = span(ws, (int64_t)need);
+    if (overlap(sY, sw)) return Q4K_ERR_ALIAS;
+    for (int j = 0; j < 4; ++j)
+        if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
+    hipStream_t s = as_stream(stream);
+    float *h = (float *)ws;
+    for (int64_t t = 0; t < seq; ++t) {
+        int st = hip_status(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                                X + t * hidden, h, inter, hidden, act, s));
+        if (st != Q4K_OK) return st;
+        st = hip_status(q4k::launch_rows_store((const uint8_t *)Wd, h, Y + t * hidden, nullptr,
+                                               nullptr, hidden, inter, hidden, hidden, s));
+        if (st != Q4K_OK) return st;
+    }
+    return Q4K_OK;
+}

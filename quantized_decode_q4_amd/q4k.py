@@ -1,0 +1,179 @@
+"""Thin ctypes binding of libq4k.so (include/q4k.h): argument marshalling only.
+
+Each function takes torch tensors (device memory) or raw integer device
+pointers, passes their addresses, sizes and the current HIP stream to the C
+call of the same name, and raises Q4KError on a nonzero status. Every step of
+the computation runs in the library's HIP kernels. There is no fallback: if
+libq4k.so is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq4k.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "q4k.h")
+
+Q4K_OK = 0
+Q4K_ERR_NULL = -1
+Q4K_ERR_SHAPE = -2
+Q4K_ERR_ALIGN = -3
+Q4K_ERR_K = -4
+Q4K_ERR_ACT = -5
+Q4K_ERR_WORKSPACE = -6
+Q4K_ERR_ALIAS = -7
+Q4K_ERR_HIP = -8
+Q4K_ACT_GELU_TANH = 0
+Q4K_ACT_SILU = 1
+Q4K_TOPK_MAX = 64
+Q4K_COLS_MAX = 65536
+
+# torch brings its own HIP runtime (same soname, libamdhip64.so.7). Loading it
+# first makes this library bind to that runtime instead of a second copy from
+# /opt/rocm: one process must use one HIP runtime, or tensors allocated by torch
+# are invisible to our launches.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                      "or python -m quantized_decode_q4_amd.build")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_INT = ctypes.c_int
+
+lib = ctypes.CDLL(LIB_PATH)
+_SIGS = {
+    "q4k_matvec": ([_P, _P, _P, _I64, _I64, _P], _INT),
+    "q4k_qkv": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "q4k_gate_up": ([_P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
+    "q4k_ffn_workspace_bytes": ([_I64, _I64], _SZ),
+    "q4k_ffn": ([_P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P], _INT),
+    "q4k_lmhead_workspace_bytes": ([_I64, _I64, _INT], _SZ),
+    "q4k_lmhead_topk": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _SZ, _P], _INT),
+    "q4k_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "q4k_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "q4k_ffn_prefill_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "q4k_ffn_prefill": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P], _INT),
+    "q4k_status_string": ([_INT], ctypes.c_char_p),
+    "q4k_last_hip_error": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+class Q4KError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.q4k_status_string(status).decode()
+        if status == Q4K_ERR_HIP:
+            msg += " -- " + lib.q4k_last_hip_error().decode()
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check(status: int, where: str) -> None:
+    if status != Q4K_OK:
+        raise Q4KError(status, where)
+
+
+def q4k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
+    _check(lib.q4k_matvec(_ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)), "q4k_matvec")
+
+
+def q4k_qkv(Wqkv, x, q, k, v, q_rows: int, kv_rows: int, cols: int, stream=None) -> None:
+    _check(lib.q4k_qkv(_ptr(Wqkv), _ptr(x), _ptr(q), _ptr(k), _ptr(v), q_rows, kv_rows, cols,
+                       _stream(stream)), "q4k_qkv")
+
+
+def q4k_gate_up(Wg, Wu, x, h, inter: int, hidden: int, act: int = Q4K_ACT_GELU_TANH,
+                stream=None) -> None:
+    _check(lib.q4k_gate_up(_ptr(Wg), _ptr(Wu), _ptr(x), _ptr(h), inter, hidden, act,
+                           _stream(stream)), "q4k_gate_up")
+
+
+def q4k_ffn_workspace_bytes(hidden: int, inter: int) -> int:
+    return lib.q4k_ffn_workspace_bytes(hidden, inter)
+
+
+def q4k_ffn(Wg, Wu, Wd, x, y, hidden: int, inter: int, act: int, ws, ws_bytes: int | None = None,
+            stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = _nbytes(ws)
+    _check(lib.q4k_ffn(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(x), _ptr(y), hidden, inter, act,
+                       _ptr(ws), ws_bytes, _stream(stream)), "q4k_ffn")
+
+
+def q4k_lmhead_workspace_bytes(rows: int, cols: int, k: int) -> int:
+    return lib.q4k_lmhead_workspace_bytes(rows, cols, k)
+
+
+def q4k_lmhead_topk(W, x, logits, rows: int, cols: int, k: int, top_idx, top_val, ws,
+                    ws_bytes: int | None = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = _nbytes(ws)
+    _check(lib.q4k_lmhead_topk(_ptr(W), _ptr(x), _ptr(logits), rows, cols, k, _ptr(top_idx),
+                               _ptr(top_val), _ptr(ws), ws_bytes, _stream(stream)),
+           "q4k_lmhead_topk")
+
+
+def q4k_matmul_workspace_bytes(rows: int, cols: int, seq: int) -> int:
+    return lib.q4k_matmul_workspace_bytes(rows, cols, seq)
+
+
+def q4k_matmul(W, X, Y, rows: int, cols: int, seq: int, ws=None, ws_bytes: int | None = None,
+               stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else _nbytes(ws)
+    _check(lib.q4k_matmul(_ptr(W), _ptr(X), _ptr(Y), rows, cols, seq, _ptr(ws), ws_bytes,
+                          _stream(stream)), "q4k_matmul")
+
+
+def q4k_ffn_prefill_workspace_bytes(seq: int, hidden: int, inter: int) -> int:
+    return lib.q4k_ffn_prefill_workspace_bytes(seq, hidden, inter)
+
+
+def q4k_ffn_prefill(Wg, Wu, Wd, X, Y, seq: int, hidden: int, inter: int, act: int, ws,
+                    ws_bytes: int | None = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = _nbytes(ws)
+    _check(lib.q4k_ffn_prefill(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(X), _ptr(Y), seq, hidden, inter,
+                               act, _ptr(ws), ws_bytes, _stream(stream)), "q4k_ffn_prefill")
+
+
+def q4k_status_string(status: int) -> str:
+    return lib.q4k_status_string(status).decode()
+
+
+def q4k_last_hip_error() -> str:
+    return lib.q4k_last_hip_error().decode()
+
+
+def workspace(nbytes: int, device="cuda"):
+    """A caller-owned device workspace of nbytes (uint8, 256-byte aligned by torch)."""
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)

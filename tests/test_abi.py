@@ -1,0 +1,135 @@
+"""The C-ABI library: loads, exports every declared symbol, and rejects bad
+arguments before touching the device (CPU only: no call here reaches a launch;
+pointers are fake, never dereferenced, because every call fails validation)."""
+import ctypes
+import re
+
+import pytest
+
+from quantized_decode_q4_amd import q4k
+
+# Fake device addresses: 256-byte aligned and far apart (never dereferenced).
+A = 0x7F0000000000
+B = 0x7F1000000000
+C = 0x7F2000000000
+D = 0x7F3000000000
+E = 0x7F4000000000
+F = 0x7F5000000000
+S = None  # stream
+
+
+def declared_functions():
+    text = open(q4k.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4k_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["q4k_matvec", "q4k_qkv", "q4k_ffn", "q4k_gate_up", "q4k_lmhead_topk", "q4k_matmul",
+              "q4k_ffn_prefill", "q4k_status_string", "q4k_last_hip_error",
+              "q4k_ffn_workspace_bytes", "q4k_lmhead_workspace_bytes",
+              "q4k_matmul_workspace_bytes", "q4k_ffn_prefill_workspace_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(q4k.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_library_exports_nothing_else():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", q4k.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
+def test_status_strings():
+    for s in range(-8, 1):
+        assert q4k.q4k_status_string(s)
+    assert "unknown" in q4k.q4k_status_string(-99)
+    assert q4k.q4k_last_hip_error() == ""
+
+
+L = q4k.lib
+
+
+def test_matvec_validation():
+    assert L.q4k_matvec(A, B, C, 10, 300, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_matvec(A, B, C, 10, 0, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_matvec(A, B, C, -1, 256, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_matvec(A, B, C, 10, 65536 + 256, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_matvec(A, B, C, 0, 256, S) == q4k.Q4K_OK            # empty: no-op
+    assert L.q4k_matvec(None, B, C, 0, 256, S) == q4k.Q4K_OK
+    assert L.q4k_matvec(None, B, C, 10, 256, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_matvec(A, None, C, 10, 256, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_matvec(A, B, None, 10, 256, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_matvec(A + 8, B, C, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert L.q4k_matvec(A, B + 4, C, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert L.q4k_matvec(A, B, C + 2, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    # y inside W, y overlapping x
+    assert L.q4k_matvec(A, B, A + 144, 10, 256, S) == q4k.Q4K_ERR_ALIAS
+    assert L.q4k_matvec(A, B, B + 1020, 10, 256, S) == q4k.Q4K_ERR_ALIAS
+    # y just past the end of W: no overlap, but do not launch (fake pointers);
+    # check only that the boundary computation is half-open via qkv below.
+
+
+def test_qkv_validation():
+    assert L.q4k_qkv(A, B, C, D, E, -1, 2, 256, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_qkv(A, B, C, D, E, 0, 0, 256, S) == q4k.Q4K_OK
+    assert L.q4k_qkv(A, B, None, D, E, 4, 2, 256, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_qkv(A, B, C, None, E, 4, 2, 256, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_qkv(A, B, C, D, E + 2, 4, 2, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert L.q4k_qkv(A, B, C, C + 8, E, 4, 2, 256, S) == q4k.Q4K_ERR_ALIAS   # k inside q
+    assert L.q4k_qkv(A, B, C, D, D + 4, 4, 2, 256, S) == q4k.Q4K_ERR_ALIAS   # v overlaps k
+
+
+def test_gate_up_and_ffn_validation():
+    assert L.q4k_gate_up(A, B, C, D, 8, 256, 2, S) == q4k.Q4K_ERR_ACT
+    assert L.q4k_gate_up(A, B, C, D, 8, 200, 0, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_gate_up(A, B, C, D, 0, 256, 0, S) == q4k.Q4K_OK
+    assert L.q4k_gate_up(A, None, C, D, 8, 256, 0, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_gate_up(A, B, C, B + 16, 8, 256, 1, S) == q4k.Q4K_ERR_ALIAS
+    need = q4k.q4k_ffn_workspace_bytes(256, 512)
+    assert need >= 512 * 4 and need % 256 == 0
+    assert q4k.q4k_ffn_workspace_bytes(256, 100) == 0
+    assert L.q4k_ffn(A, B, C, D, E, 256, 512, 0, F, need - 1, S) == q4k.Q4K_ERR_WORKSPACE
+    assert L.q4k_ffn(A, B, C, D, E, 256, 512, 0, None, need, S) == q4k.Q4K_ERR_WORKSPACE
+    assert L.q4k_ffn(A, B, C, D, E, 256, 512, 0, F + 8, need, S) == q4k.Q4K_ERR_ALIGN
+    assert L.q4k_ffn(A, B, C, D, E, 256, 512, 5, F, need, S) == q4k.Q4K_ERR_ACT
+    assert L.q4k_ffn(A, B, C, D, F, 256, 512, 0, F, need, S) == q4k.Q4K_ERR_ALIAS   # y in ws
+    assert L.q4k_ffn(A, B, C, D, E, 256, 512, 0, D, need, S) == q4k.Q4K_ERR_ALIAS   # ws on x
+
+
+def test_lmhead_validation():
+    need = q4k.q4k_lmhead_workspace_bytes(1000, 256, 5)
+    assert need > 0 and need % 256 == 0
+    assert q4k.q4k_lmhead_workspace_bytes(1000, 256, 0) == 0
+    assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 0, D, E, F, need, S) == q4k.Q4K_ERR_K
+    assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 65, D, E, F, need, S) == q4k.Q4K_ERR_K
+    assert L.q4k_lmhead_topk(A, B, C, 4, 256, 5, D, E, F, need, S) == q4k.Q4K_ERR_K
+    assert L.q4k_lmhead_topk(A, B, C, 0, 256, 1, D, E, F, need, S) == q4k.Q4K_ERR_K
+    assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, E, F, need - 8, S) == q4k.Q4K_ERR_WORKSPACE
+    assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, None, E, F, need, S) == q4k.Q4K_ERR_NULL
+    assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, D + 8, F, need, S) == q4k.Q4K_ERR_ALIAS
+    assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, E, C + 64, need, S) == q4k.Q4K_ERR_ALIAS
+    # a vocabulary too large for the single-workgroup merge at k = 64
+    assert L.q4k_lmhead_topk(A, B, C, 4_000_000, 256, 64, D, E, F, 1 << 40, S) == q4k.Q4K_ERR_SHAPE
+
+
+def test_prefill_validation():
+    assert q4k.q4k_matmul_workspace_bytes(512, 2560, 63) == 0
+    assert q4k.q4k_matmul_workspace_bytes(512, 2560, 64) >= 64 * 2560 * 2
+    assert L.q4k_matmul(A, B, C, 10, 256, -1, None, 0, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_matmul(A, B, C, 10, 256, 0, None, 0, S) == q4k.Q4K_OK
+    assert L.q4k_matmul(A, B, C, 10, 256, 64, None, 0, S) == q4k.Q4K_ERR_WORKSPACE
+    assert L.q4k_matmul(A, B, B + 64, 10, 256, 2, None, 0, S) == q4k.Q4K_ERR_ALIAS
+    need = q4k.q4k_ffn_prefill_workspace_bytes(64, 256, 512)
+    assert need >= 64 * 256 * 2 + 64 * 512 * 2
+    assert L.q4k_ffn_prefill(A, B, C, D, E, 64, 256, 512, 3, F, need, S) == q4k.Q4K_ERR_ACT
+    assert L.q4k_ffn_prefill(A, B, C, D, E, 64, 256, 512, 0, F, need - 1, S) == q4k.Q4K_ERR_WORKSPACE
+    assert L.q4k_ffn_prefill(A, B, C, D, E, 0, 256, 512, 0, None, 0, S) == q4k.Q4K_OK
+    assert L.q4k_ffn_prefill(A, B, C, D, F + 256, 64, 256, 512, 0, F, need, S) == q4k.Q4K_ERR_ALIAS

@@ -1,0 +1,357 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Pass rule for the f32 paths, per output element: |gpu - oracle| <= 1e-4 * A,
+A = sum_j |w_ij x_j| from the oracle. Top-k indices must match exactly except
+where two candidates are indistinguishable at that tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+from quantized_decode_q4_amd import inputs
+from q4k_fields import Fields, pack_block
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def q4k():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_decode_q4_amd import q4k as mod
+    return mod
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def ratio(got, ref, A):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(A > 0, err / A, np.where(err == 0, 0.0, np.inf))
+    return float(r.max()) if r.size else 0.0
+
+
+def assert_close(got, ref, A, tol=TOL, what=""):
+    r = ratio(got, ref, A)
+    print(f"{what}: max |err|/A = {r:.3e}", flush=True)
+    assert r <= tol, f"{what}: max |err|/A = {r:.3e} > {tol}"
+
+
+def gpu_matvec(q4k, W, x, rows, cols):
+    y = torch.full((rows,), float("nan"), device="cuda")
+    q4k.q4k_matvec(dev(W), dev(x), y, rows, cols)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ matvec ---
+
+def test_tiny_matvec_config(q4k, orc):
+    c = inputs.tiny_matvec()
+    y = gpu_matvec(q4k, c["W"], c["x"], 256, 512)
+    ref, A = orc.matvec(c["W"], c["x"], 256, 512)
+    assert_close(y, ref, A, what="tiny 256x512")
+
+
+def test_single_hot_probes_recover_every_weight(q4k, orc):
+    """x = e_j for every column j of the tiny workload gives column j of the
+    dequantised matrix: the GPU's reading of the byte layout, element by element."""
+    c = inputs.tiny_matvec()
+    dense = orc.dequant(c["W"], 256, 512)
+    dW = dev(c["W"])
+    X = torch.eye(512, dtype=torch.float32, device="cuda")
+    Y = torch.empty((512, 256), device="cuda")
+    for j in range(512):
+        q4k.q4k_matvec(dW, X[j], Y[j], 256, 512)
+    torch.cuda.synchronize()
+    got = Y.cpu().numpy().T.astype(np.float64)
+    rel = np.abs(got - dense) / np.maximum(np.abs(dense), 1e-30)
+    assert np.all(np.abs(got - dense) <= TOL * np.abs(dense))
+    assert rel.max() < 1e-6, rel.max()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 256), (7, 256), (33, 768), (100, 1280), (1000, 2560),
+                                       (257, 4096), (65, 10240), (3, 40960), (5, 65536),
+                                       (513, 2304), (40, 512)])
+def test_matvec_ragged_shapes(q4k, orc, rows, cols):
+    rng = np.random.default_rng(rows * 7919 + cols)
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    y = gpu_matvec(q4k, W, x, rows, cols)
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(y, ref, A, what=f"matvec {rows}x{cols}")
+
+
+def test_matvec_crafted_fields(q4k, orc):
+    """Zero nibbles, zero d, saturated fields and extreme binary16 scales."""
+    rng = np.random.default_rng(21)
+    rows, cols = 24, 1024
+    cases = [Fields(rng, rows, cols, q=np.zeros(256, int)),
+             Fields(rng, rows, cols, d=0.0),
+             Fields(rng, rows, cols, dmin=0.0, sc=np.full(8, 63), q=np.full(256, 15)),
+             Fields(rng, rows, cols, mn=np.full(8, 63), sc=np.zeros(8, int))]
+    for F in cases:
+        W = F.to_bytes()
+        x = inputs.normal_f32(rng, cols)
+        y = gpu_matvec(q4k, W, x, rows, cols)
+        ref, A = orc.matvec(W, x, rows, cols)
+        assert_close(y, ref, A, what="crafted")
+    # subnormal / large binary16 d and dmin
+    blocks = []
+    for i in range(rows * 4):
+        d_bits = [0x0001, 0x03FF, 0x0400, 0x3C00, 0x5BFF][i % 5]
+        m_bits = [0x7800, 0x0001, 0x2E66, 0x0200, 0x1400][(i // 5) % 5]
+        blocks.append(pack_block(np.uint16(d_bits), np.uint16(m_bits), rng.integers(0, 64, 8),
+                                 rng.integers(0, 64, 8), rng.integers(0, 16, 256)))
+    W = np.stack(blocks).reshape(rows, 4 * 144)
+    x = inputs.normal_f32(rng, cols)
+    y = gpu_matvec(q4k, W, x, rows, cols)
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(y, ref, A, what="extreme f16")
+
+
+def test_matvec_deterministic_and_on_side_stream(q4k, orc):
+    rng = np.random.default_rng(22)
+    rows, cols = 3000, 2560
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    dW, dx = dev(W), dev(x)
+    s = torch.cuda.Stream()
+    ys = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            y = torch.empty(rows, device="cuda")
+            q4k.q4k_matvec(dW, dx, y, rows, cols)
+            ys.append(y)
+    s.synchronize()
+    a = ys[0].cpu().numpy()
+    for y in ys[1:]:
+        assert np.array_equal(a.view(np.uint32), y.cpu().numpy().view(np.uint32))
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(a, ref, A, what="side stream")
+
+
+# --------------------------------------------------------------------- QKV ---
+
+def test_qkv_config(q4k, orc):
+    c = inputs.qkv()
+    qr, kr, cols = c["q_rows"], c["kv_rows"], 2560
+    q = torch.empty(qr, device="cuda")
+    k = torch.empty(kr, device="cuda")
+    v = torch.empty(kr, device="cuda")
+    q4k.q4k_qkv(dev(c["W"]), dev(c["x"]), q, k, v, qr, kr, cols)
+    torch.cuda.synchronize()
+    ref, A = orc.matvec(c["W"], c["x"], qr + 2 * kr, cols)
+    assert_close(q.cpu().numpy(), ref[:qr], A[:qr], what="q")
+    assert_close(k.cpu().numpy(), ref[qr:qr + kr], A[qr:qr + kr], what="k")
+    assert_close(v.cpu().numpy(), ref[qr + kr:], A[qr + kr:], what="v")
+
+
+@pytest.mark.parametrize("qr,kr", [(8, 3), (1, 0), (0, 5), (37, 11)])
+def test_qkv_splits(q4k, orc, qr, kr):
+    rng = np.random.default_rng(qr * 100 + kr)
+    cols = 512
+    rows = qr + 2 * kr
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    q = torch.full((max(qr, 1),), float("nan"), device="cuda")
+    k = torch.full((max(kr, 1),), float("nan"), device="cuda")
+    v = torch.full((max(kr, 1),), float("nan"), device="cuda")
+    q4k.q4k_qkv(dev(W), dev(x), q, k, v, qr, kr, cols)
+    torch.cuda.synchronize()
+    ref, A = orc.matvec(W, x, rows, cols)
+    got = np.concatenate([q.cpu().numpy()[:qr], k.cpu().numpy()[:kr], v.cpu().numpy()[:kr]])
+    assert_close(got, ref, A, what=f"qkv {qr}/{kr}")
+
+
+# --------------------------------------------------------------------- FFN ---
+
+def _h_tolerance(orc, Wg, Wu, x, inter, hidden, act):
+    g, Ag = orc.matvec(Wg, x, inter, hidden)
+    u, Au = orc.matvec(Wu, x, inter, hidden)
+    a = orc.act_array(g, act)
+    # |d act/dz| <= 1.13 (GELU-tanh) and <= 1.1 (SiLU)
+    return a * u, 1.2 * np.abs(u) * Ag + np.abs(a) * Au
+
+
+def test_gate_up_h_config_layer0(q4k, orc):
+    L = inputs.ffn_layer(0)
+    hidden, inter = 2560, 10240
+    h = torch.empty(inter, device="cuda")
+    q4k.q4k_gate_up(dev(L["Wg"]), dev(L["Wu"]), dev(L["x"]), h, inter, hidden,
+                    q4k.Q4K_ACT_GELU_TANH)
+    torch.cuda.synchronize()
+    ref, Ah = _h_tolerance(orc, L["Wg"], L["Wu"], L["x"], inter, hidden, orc.GELU_TANH)
+    assert_close(h.cpu().numpy(), ref, Ah, what="h layer 0")
+
+
+def test_ffn_all_34_layers(q4k, orc):
+    hidden, inter = 2560, 10240
+    ws = q4k.workspace(q4k.q4k_ffn_workspace_bytes(hidden, inter))
+    worst = 0.0
+    for layer in range(inputs.N_LAYERS):
+        L = inputs.ffn_layer(layer)
+        y = torch.empty(hidden, device="cuda")
+        q4k.q4k_ffn(dev(L["Wg"]), dev(L["Wu"]), dev(L["Wd"]), dev(L["x"]), y, hidden, inter,
+                    q4k.Q4K_ACT_GELU_TANH, ws)
+        torch.cuda.synchronize()
+        r = orc.ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], hidden, inter, orc.GELU_TANH)
+        rr = ratio(y.cpu().numpy(), r["y"], r["A"])
+        worst = max(worst, rr)
+        assert rr <= TOL, (layer, rr)
+    print(f"ffn 34 layers: worst |err|/A = {worst:.3e}")
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("hidden,inter", [(256, 256), (512, 1280), (768, 2304)])
+def test_ffn_small_shapes_both_activations(q4k, orc, act, hidden, inter):
+    rng = np.random.default_rng(hidden + inter + act)
+    Wg = inputs.q4k_random(rng, inter, hidden)
+    Wu = inputs.q4k_random(rng, inter, hidden)
+    Wd = inputs.q4k_random(rng, hidden, inter)
+    x = inputs.normal_f32(rng, hidden)
+    y = torch.empty(hidden, device="cuda")
+    ws = q4k.workspace(q4k.q4k_ffn_workspace_bytes(hidden, inter))
+    q4k.q4k_ffn(dev(Wg), dev(Wu), dev(Wd), dev(x), y, hidden, inter, act, ws)
+    torch.cuda.synchronize()
+    r = orc.ffn(Wg, Wu, Wd, x, hidden, inter, act)
+    assert_close(y.cpu().numpy(), r["y"], r["A"], what=f"ffn act={act} {hidden}/{inter}")
+
+
+# ------------------------------------------------------------------ lm_head ---
+
+def topk_ok(gpu_idx, gpu_val, ref_logits, A, k):
+    """Exact index match, except that a swap between candidates whose oracle
+    logits are within the fp32 tolerance of each other is accepted."""
+    ridx, _ = orcmod().topk(ref_logits, k)
+    for r in range(k):
+        gi, oi = int(gpu_idx[r]), int(ridx[r])
+        if gi == oi:
+            continue
+        gap = abs(ref_logits[gi] - ref_logits[oi])
+        assert gap <= TOL * (A[gi] + A[oi]), (r, gi, oi, gap)
+    assert len(set(int(i) for i in gpu_idx)) == k
+
+
+def orcmod():
+    import oracle
+    return oracle
+
+
+def gpu_lmhead(q4k, W, x, rows, cols, k):
+    logits = torch.empty(rows, device="cuda")
+    ti = torch.empty(k, dtype=torch.int32, device="cuda")
+    tv = torch.empty(k, device="cuda")
+    ws = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(rows, cols, k))
+    q4k.q4k_lmhead_topk(dev(W), dev(x), logits, rows, cols, k, ti, tv, ws)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), ti.cpu().numpy(), tv.cpu().numpy()
+
+
+def test_lmhead_config_top5(q4k, orc):
+    c = inputs.lm_head()
+    rows, cols = inputs.VOCAB, inputs.HIDDEN
+    logits, ti, tv = gpu_lmhead(q4k, c["W"], c["x"], rows, cols, 5)
+    ref, A = orc.matvec(c["W"], c["x"], rows, cols)
+    assert_close(logits, ref, A, what="lm_head logits")
+    topk_ok(ti, tv, ref, A, 5)
+    # values are the GPU logits at those rows
+    assert np.array_equal(tv.view(np.uint32), logits[ti].view(np.uint32))
+    ridx, rval = orc.topk(ref, 5)
+    print("top-5 gpu", ti.tolist(), tv.tolist(), "oracle", ridx.tolist(), rval.tolist())
+
+
+@pytest.mark.parametrize("rows,cols,k", [(1, 256, 1), (64, 512, 64), (100, 256, 7),
+                                         (4097, 512, 64), (30000, 1024, 5), (20000, 768, 33)])
+def test_lmhead_shapes_and_k(q4k, orc, rows, cols, k):
+    rng = np.random.default_rng(rows + cols + k)
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols, scale=1 / np.sqrt(cols))
+    logits, ti, tv = gpu_lmhead(q4k, W, x, rows, cols, k)
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(logits, ref, A, what=f"lm_head {rows}x{cols}")
+    topk_ok(ti, tv, ref, A, k)
+    # the GPU's own ranking of its logits is exactly (value desc, index asc)
+    gidx, _ = orc.topk(logits.astype(np.float64), k)
+    assert np.array_equal(ti, gidx)
+
+
+def test_lmhead_duplicated_rows_tie_break(q4k, orc):
+    rng = np.random.default_rng(31)
+    rows, cols = 9000, 512
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    ref, _ = orc.matvec(W, x, rows, cols)
+    best = int(np.argmax(ref))
+    for r in (8999, 4500, 3, best + 1 if best + 1 < rows else 0):
+        W[r] = W[best]
+    logits, ti, tv = gpu_lmhead(q4k, W, x, rows, cols, 6)
+    dup = sorted({best, 8999, 4500, 3, best + 1 if best + 1 < rows else 0})
+    assert ti[:len(dup)].tolist() == dup
+    assert len(set(tv[:len(dup)].view(np.uint32).tolist())) == 1
+
+
+def test_lmhead_nan_rows_rank_last(q4k, orc):
+    rng = np.random.default_rng(32)
+    rows, cols = 300, 256
+    W = inputs.q4k_random(rng, rows, cols)
+    nan_rows = [0, 5, 299]
+    for r in nan_rows:
+        W[r, 0:2] = np.array([0x00, 0x7E], np.uint8)   # d = binary16 NaN
+    x = inputs.normal_f32(rng, cols)
+    logits, ti, tv = gpu_lmhead(q4k, W, x, rows, cols, 10)
+    assert np.all(np.isnan(logits[nan_rows]))
+    assert not set(ti.tolist()) & set(nan_rows)
+    # k = rows: NaN rows come last, in index order
+    logits, ti, tv = gpu_lmhead(q4k, W[:12], x, 12, cols, 12)
+    assert ti[-2:].tolist() == [0, 5]
+    ref, _ = orc.matvec(W[:12], x, 12, cols)
+    ridx, _ = orc.topk(ref, 12)
+    assert ti.tolist() == ridx.tolist()
+
+
+# ----------------------------------------------------------------- prefill ---
+
+def test_matmul_small_seq_matches_per_token_oracle(q4k, orc):
+    rng = np.random.default_rng(41)
+    rows, cols, seq = 300, 1024, 5
+    W = inputs.q4k_random(rng, rows, cols)
+    X = inputs.normal_f32(rng, (seq, cols))
+    Y = torch.empty((seq, rows), device="cuda")
+    q4k.q4k_matmul(dev(W), dev(X), Y, rows, cols, seq)
+    torch.cuda.synchronize()
+    ref, A = orc.matmul(W, X, rows, cols)
+    assert_close(Y.cpu().numpy(), ref, A, what="matmul seq=5")
+
+
+def test_ffn_prefill_small_seq(q4k, orc):
+    rng = np.random.default_rng(42)
+    hidden, inter, seq = 512, 768, 3
+    Wg = inputs.q4k_random(rng, inter, hidden)
+    Wu = inputs.q4k_random(rng, inter, hidden)
+    Wd = inputs.q4k_random(rng, hidden, inter)
+    X = inputs.normal_f32(rng, (seq, hidden))
+    Y = torch.empty((seq, hidden), device="cuda")
+    ws = q4k.workspace(q4k.q4k_ffn_prefill_workspace_bytes(seq, hidden, inter))
+    q4k.q4k_ffn_prefill(dev(Wg), dev(Wu), dev(Wd), dev(X), Y, seq, hidden, inter, 0, ws)
+    torch.cuda.synchronize()
+    ref, A = orc.ffn_prefill(Wg, Wu, Wd, X, hidden, inter, 0)
+    assert_close(Y.cpu().numpy(), ref, A, what="ffn_prefill seq=3")
+
+
+def test_errors_raise_and_enqueue_nothing(q4k):
+    y = torch.full((10,), 7.0, device="cuda")
+    W = torch.zeros(10 * 144, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(256, device="cuda")
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_matvec(W, x, y, 10, 300)
+    assert e.value.status == q4k.Q4K_ERR_SHAPE
+    with pytest.raises(q4k.Q4KError):
+        q4k.q4k_matvec(W, x, W, 10, 256)          # output aliases W
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
