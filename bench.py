@@ -1,0 +1,321 @@
+"""Benchmark of the Q4_K decode hot path on one MI355X.
+
+A step is one decoded token's Q4_K work at Gemma-3-4B shapes: for each of 34
+independently seeded layers the fused QKV projection (4096 x 2560) and the
+gated FFN (gate+up 2 x 10240 x 2560 -> GELU-tanh -> down 2560 x 10240), then the
+lm_head (262144 x 2560) with top-5. All weights (2.1 GB) are resident in HBM
+before timing; 34 distinct layers exceed the 256 MB Infinity Cache, so each
+step streams its weights from HBM. Steps are replayed from HIP graphs captured
+once (launch-bound inner loop); the eager launch rate is reported beside it.
+
+Prints ONE JSON line (see the fields at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+BYTES_PER_WEIGHT = 144 / 256   # Q4_K: 4.5 bits per weight
+
+HIDDEN, INTER, QROWS, KVROWS, VOCAB, LAYERS, TOPK = 2560, 10240, 2048, 1024, 262144, 34, 5
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def wbytes(rows: int, cols: int) -> int:
+    return rows * cols // 256 * 144
+
+
+# Algorithmic bytes: weights once + activations in + outputs out (f32).
+QKV_BYTES = wbytes(QROWS + 2 * KVROWS, HIDDEN) + HIDDEN * 4 + (QROWS + 2 * KVROWS) * 4
+GATE_UP_BYTES = 2 * wbytes(INTER, HIDDEN) + HIDDEN * 4 + INTER * 4
+DOWN_BYTES = wbytes(HIDDEN, INTER) + INTER * 4 + HIDDEN * 4
+LAYER_BYTES = QKV_BYTES + GATE_UP_BYTES + DOWN_BYTES
+LMHEAD_BYTES = wbytes(VOCAB, HIDDEN) + HIDDEN * 4 + VOCAB * 4 + TOPK * 8
+STEP_BYTES = LAYERS * LAYER_BYTES + LMHEAD_BYTES
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_decode_q4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
+    summary, if it was taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(data, budget_s: float):
+    """The oracle (single-threaded C, f64) on a bounded sample of the step:
+    whole decode layers (QKV + FFN) in order until the time budget is spent,
+    plus a slice of lm_head rows; GB/s of algorithmic bytes processed."""
+    import oracle
+    t0 = time.perf_counter()
+    done_bytes = 0
+    layers = 0
+    for l in range(LAYERS):
+        c = data["qkv_host"][l]
+        oracle.matvec(c["W"], c["x"], QROWS + 2 * KVROWS, HIDDEN)
+        L = data["ffn_host"][l]
+        oracle.ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], HIDDEN, INTER, oracle.GELU_TANH)
+        done_bytes += LAYER_BYTES
+        layers += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    lm_rows = 16384
+    lm = data["lm_host"]
+    oracle.matvec(lm["W"][:lm_rows], lm["x"], lm_rows, HIDDEN)
+    done_bytes += wbytes(lm_rows, HIDDEN) + HIDDEN * 4 + lm_rows * 4
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{layers} decode layers (fused QKV + gate/up/down FFN) + {lm_rows} of "
+                      f"{VOCAB} lm_head rows, single-threaded f64 C oracle, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--kernel-only", default="", help="launch only this part (profiling): "
+                    "gate_up | down | qkv | lmhead")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; sharding is described in the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    from quantized_decode_q4_amd import inputs
+    from quantized_decode_q4_amd import q4k
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} CUs={props.multi_processor_count}")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.perf_counter()
+    qkv_host, ffn_host, qkv_dev, ffn_dev = [], [], [], []
+    for l in range(LAYERS):
+        c = inputs.qkv(copy=l)
+        L = inputs.ffn_layer(l)
+        qkv_dev.append({"W": up(c["W"]), "x": up(c["x"])})
+        ffn_dev.append({k: up(L[k]) for k in ("Wg", "Wu", "Wd", "x")})
+        if not args.no_cpu:
+            qkv_host.append(c)
+            ffn_host.append(L)
+        if l % 8 == 7:
+            log(f"generated {l + 1}/{LAYERS} layers ({time.perf_counter() - t0:.1f}s)")
+    lm = inputs.lm_head()
+    lm_dev = {"W": up(lm["W"]), "x": up(lm["x"])}
+    torch.cuda.synchronize()
+    log(f"inputs resident: {(LAYERS * (QKV_BYTES + GATE_UP_BYTES + DOWN_BYTES) + LMHEAD_BYTES) / 1e9:.2f} GB "
+        f"({time.perf_counter() - t0:.1f}s)")
+
+    q = torch.empty(QROWS, device=dev)
+    k = torch.empty(KVROWS, device=dev)
+    v = torch.empty(KVROWS, device=dev)
+    y = torch.empty(HIDDEN, device=dev)
+    h = q4k.workspace(q4k.q4k_ffn_workspace_bytes(HIDDEN, INTER))
+    logits = torch.empty(VOCAB, device=dev)
+    top_idx = torch.empty(TOPK, dtype=torch.int32, device=dev)
+    top_val = torch.empty(TOPK, device=dev)
+    lm_ws = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(VOCAB, HIDDEN, TOPK))
+    GELU = q4k.Q4K_ACT_GELU_TANH
+
+    def run_layers():
+        for l in range(LAYERS):
+            c, L = qkv_dev[l], ffn_dev[l]
+            q4k.q4k_qkv(c["W"], c["x"], q, k, v, QROWS, KVROWS, HIDDEN)
+            q4k.q4k_ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], y, HIDDEN, INTER, GELU, h)
+
+    def run_lmhead():
+        q4k.q4k_lmhead_topk(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx, top_val,
+                            lm_ws)
+
+    if args.kernel_only:
+        # profiling helper: launch one kind of kernel over the 34 layers
+        parts = {
+            "gate_up": lambda: [q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], h, INTER, HIDDEN, GELU)
+                                for L in ffn_dev],
+            "down": lambda: [q4k.q4k_matvec(L["Wd"], h, y, HIDDEN, INTER) for L in ffn_dev],
+            "qkv": lambda: [q4k.q4k_qkv(c["W"], c["x"], q, k, v, QROWS, KVROWS, HIDDEN)
+                            for c in qkv_dev],
+            "lmhead": run_lmhead,
+        }
+        fn = parts[args.kernel_only]
+        for i in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        log(f"kernel-only {args.kernel_only}: {args.warmup + args.steps} passes done")
+        return 0
+
+    # ------------------------------------------------------- eager + graphs
+    run_layers()
+    run_lmhead()
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        g_layers = torch.cuda.CUDAGraph()
+        g_lm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_layers):
+            run_layers()
+        with torch.cuda.graph(g_lm):
+            run_lmhead()
+        torch.cuda.synchronize()
+        step_layers, step_lm = g_layers.replay, g_lm.replay
+    else:
+        step_layers, step_lm = run_layers, run_lmhead
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step_layers()
+        step_lm()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done (graph={use_graph})")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step_layers()
+        ev[i][1].record(stream)
+        step_lm()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    layers_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    lm_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
+    med_layers_ms = layers_ms[len(layers_ms) // 2]
+    med_lm_ms = lm_ms[len(lm_ms) // 2]
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; layers {med_layers_ms:.3f} ms, "
+        f"lm_head {med_lm_ms:.3f} ms (median)")
+
+    # eager launch rate of the same step, for context
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    n_eager = max(3, args.steps // 5)
+    for _ in range(n_eager):
+        run_layers()
+        run_lmhead()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - te) * 1e3 / n_eager
+
+    # ------------------------------------- dominant kernel: fused gate+up
+    reps = 5
+    per_launch = []
+    for _ in range(reps):
+        pairs = []
+        for L in ffn_dev:
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], h, INTER, HIDDEN, GELU)
+            b_ev.record(stream)
+            pairs.append((a_ev, b_ev))
+        torch.cuda.synchronize()
+        per_launch.append(sum(a.elapsed_time(b) for a, b in pairs) / len(pairs))
+    per_launch.sort()
+    gu_ms = per_launch[len(per_launch) // 2]
+    gu_gbs = GATE_UP_BYTES / (gu_ms * 1e-3) / 1e9
+    traffic = counters_traffic("gate_up")
+    log(f"gate_up: {gu_ms * 1e3:.2f} us/launch, {gu_gbs:.0f} GB/s")
+
+    # ------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline({"qkv_host": qkv_host, "ffn_host": ffn_host, "lm_host": lm},
+                           args.cpu_budget)
+        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+
+    value = STEP_BYTES / (ms_per_step * 1e-3) / 1e9
+    us_per_layer = med_layers_ms * 1e3 / LAYERS
+    rec = {
+        "metric": "Q4_K matvec HBM GB/s (% of peak) + us/decode-layer at Gemma-3-4B shapes",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "gemma3-4b decode step: 34 x (fused QKV 4096x2560 + gated FFN "
+                        "10240x2560 gate/up, 2560x10240 down, GELU-tanh) + lm_head 262144x2560 top-5, "
+                        "Q4_K weights, f32 activations",
+            "layers": LAYERS, "hidden": HIDDEN, "inter": INTER, "vocab": VOCAB, "top_k": TOPK,
+            "graph_replay": use_graph,
+            "step_bytes": STEP_BYTES,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "us_per_decode_layer": round(us_per_layer, 3),
+        "decode_layer_gbs": round(LAYER_BYTES / (us_per_layer * 1e-6) / 1e9, 1),
+        "lm_head_us": round(med_lm_ms * 1e3, 2),
+        "lm_head_gbs": round(LMHEAD_BYTES / (med_lm_ms * 1e-3) / 1e9, 1),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "roofline": {
+            "kernel": "q4k gate_up (fused gate+up + GELU-tanh), 2 x 10240x2560",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": GATE_UP_BYTES,
+            "us_per_launch": round(gu_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -163,7 +163,7 @@ Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int
     if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
     if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
     const int64_t nwg = q4k::lmhead_num_wgs(rows, cols);
-    if (nwg * k > q4k::kMergeCandMax) return Q4K_ERR_SHAPE;
+    if (nwg > q4k::kMergeListsMax) return Q4K_ERR_SHAPE;
     if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||
         !aligned(top_val, 4))

@@ -12,7 +12,7 @@ constexpr int kBlockBytes = 144;  // bytes per super-block
 constexpr int kTopkMax = 64;
 constexpr int kColsMax = 65536;
 constexpr int kLmheadRowsPerWgMax = 4096;
-constexpr int kMergeCandMax = 32768;   // candidates the single-workgroup merge holds
+constexpr int kMergeListsMax = 1024;    // per-workgroup candidate lists the merge takes
 
 // Row-streaming kernels (q4k_rows.hip).
 // y rows [0, split0) -> o0, [split0, split1) -> o1, [split1, rows) -> o2.

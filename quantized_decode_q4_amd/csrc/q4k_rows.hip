@@ -71,6 +71,16 @@ __device__ __forceinline__ float act_apply(float z, int act)
 //   nq[0..7]: the 32 quant bytes; hd: the 16-byte block header.
 // Low nibbles are A's quants; high nibbles are kept in place (16*q) and the
 // factor 1/16 is folded into B's scale (exact, a power of two).
+__device__ __forceinline__ uint32_t and_opaque(uint32_t v, uint32_t m)
+{
+    // An AND the optimiser cannot see through: the byte conversions below then
+    // stay single v_cvt_f32_ubyte{0..3} instructions instead of a bit-field
+    // extract followed by a conversion.
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(m), "v"(v));
+    return r;
+}
+
 __device__ __forceinline__ float unit_dot(const uint32_t (&nq)[8], uint4 hd,
                                           const float (&xa)[32], const float (&xb)[32],
                                           float SA, float SB, int sh, bool upper)
@@ -78,8 +88,8 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&nq)[8], uint4 hd,
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const uint32_t lo = nq[k] & 0x0F0F0F0Fu;
-        const uint32_t hi = nq[k] & 0xF0F0F0F0u;
+        const uint32_t lo = and_opaque(nq[k], 0x0F0F0F0Fu);
+        const uint32_t hi = and_opaque(nq[k], 0xF0F0F0F0u);
         a0 = fmaf((float)(lo & 0xFFu), xa[4 * k + 0], a0);
         a1 = fmaf((float)((lo >> 8) & 0xFFu), xa[4 * k + 1], a1);
         a0 = fmaf((float)((lo >> 16) & 0xFFu), xa[4 * k + 2], a0);
@@ -151,12 +161,67 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
     return m;
 }
 
-template <int RPS, int P, int NMAT, int EPI, int MAXT>
+// Unconditional 16-byte loads through a bounds-checked buffer resource: an
+// offset at or beyond the resource's size reads zeros instead of faulting, so
+// lanes with nothing to load (rows past the end, unused units) issue the same
+// instructions as the others. Every path then has the same number of loads in
+// flight, which keeps the in-order wait counts of the software pipeline exact.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// One in-flight row-unit per matrix: 32 quant bytes + the 16-byte header.
+template <int NMAT>
+struct Slot {
+    uint32_t q[NMAT][8];
+    uint4 h[NMAT];
+};
+
+// off: byte offset of the row's block header inside the workgroup's resource
+// (kOutOfRange for nothing); qoff = 16 + 32g, the unit's quant bytes.
+template <int NMAT>
+__device__ __forceinline__ void load_slot(Slot<NMAT> &sl, const __amdgpu_buffer_rsrc_t (&rs)[NMAT],
+                                          uint32_t off, uint32_t qoff)
+{
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        sl.h[m] = bload16(rs[m], off);
+        const uint4 q0 = bload16(rs[m], off + qoff);
+        const uint4 q1 = bload16(rs[m], off + qoff + 16);
+        sl.q[m][0] = q0.x; sl.q[m][1] = q0.y; sl.q[m][2] = q0.z; sl.q[m][3] = q0.w;
+        sl.q[m][4] = q1.x; sl.q[m][5] = q1.y; sl.q[m][6] = q1.z; sl.q[m][7] = q1.w;
+    }
+}
+
+// Persistent row-streaming kernel.
+//  RPS  rows per sweep (threads t = u*RPS + r own unit u of row r of a sweep)
+//  NMAT 1 (one matrix) or 2 (gate and up rows sharing the activation)
+//  EPI  epilogue: store / gated activation / logits + block top-k
+//  D    sweeps whose loads are in flight while one sweep is computed
+// Workgroup w processes the contiguous sweeps [S*w/G, S*(w+1)/G) of the
+// S = ceil(rows / RPS) sweeps. The quant/header loads of the first D sweeps
+// are issued before the activation slice, then every step issues sweep i+D
+// and computes sweep i (a register ring of D+1 slots, statically indexed by
+// unrolling). Wave partial sums go to an LDS bank; every FB sweeps one barrier
+// publishes them and threads t < FB*RPS finish the rows.
+template <int RPS, int NMAT, int EPI, int MAXT, int D>
 __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 {
     static_assert(RPS >= 1 && RPS <= 64 && (64 % RPS) == 0, "RPS must divide 64");
     constexpr int NW = MAXT / 64;
-    __shared__ float red[NW][P * NMAT * RPS];
+    constexpr int FB = 8;
+    __shared__ float red[2][NW][FB * NMAT * RPS];
     __shared__ float lg[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint8_t taken[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint64_t keys_scratch[EPI == EPI_LOGITS ? NW : 1];
@@ -171,100 +236,112 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int sh = (g & 1) * 16;
     const bool upper = g >= 2;
     const int64_t rowbytes = (int64_t)a.nb * kBlockBytes;
-    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_wg;
-    const int64_t row_end = min(row_begin + a.rows_per_wg, a.rows);
+    const int64_t unit_off = (int64_t)b * kBlockBytes;
+    const int64_t S = (a.rows + RPS - 1) / RPS;
+    const int64_t s_begin = S * blockIdx.x / gridDim.x;
+    const int64_t s_end = S * (blockIdx.x + 1) / gridDim.x;
+    const int64_t row_begin = s_begin * RPS;
+    const int64_t row_stop = min(s_end * RPS, a.rows);
+
+    // Buffer resources over this workgroup's rows (the host keeps the span
+    // below 2^31 bytes); offsets are relative to row_begin.
+    __amdgpu_buffer_rsrc_t rs[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+        rs[m] = make_rsrc((m == 0 ? a.W0 : a.W1) + row_begin * rowbytes,
+                          (uint32_t)((row_stop - row_begin) * rowbytes));
+    const uint32_t qoff = 16u + 32u * (uint32_t)g;
+    // byte offset of (sweep s, this thread's row) or kOutOfRange
+    auto slot_off = [&](int64_t sw) -> uint32_t {
+        const int64_t row = sw * RPS + r;
+        return (uact && row < row_stop) ? (uint32_t)((row - row_begin) * rowbytes + unit_off)
+                                        : kOutOfRange;
+    };
+
+    Slot<NMAT> buf[D + 1];
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_slot<NMAT>(buf[j], rs, slot_off(s_begin + j), qoff);
 
     // The thread's 64 activations: x[256b + 64g + 0..31] (sub-block A) and
-    // x[256b + 64g + 32..63] (sub-block B).
+    // x[256b + 64g + 32..63] (sub-block B), loaded once.
+    // Unused units read zeros (out-of-range offset).
     float xa[32], xb[32];
     float SA = 0.f, SB = 0.f;
-    if (uact) {
-        const float4 *xp = reinterpret_cast<const float4 *>(a.x + 256 * b + 64 * g);
+    {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.nb * 1024u);
+        const uint32_t xo = uact ? (uint32_t)(256 * b + 64 * g) * 4u : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float4 va = xp[i];
-            const float4 vb = xp[8 + i];
-            xa[4 * i + 0] = va.x; xa[4 * i + 1] = va.y; xa[4 * i + 2] = va.z; xa[4 * i + 3] = va.w;
-            xb[4 * i + 0] = vb.x; xb[4 * i + 1] = vb.y; xb[4 * i + 2] = vb.z; xb[4 * i + 3] = vb.w;
+            const uint4 va = bload16(rx, xo + 16u * i);
+            const uint4 vb = bload16(rx, xo + 128u + 16u * i);
+            xa[4 * i + 0] = __uint_as_float(va.x); xa[4 * i + 1] = __uint_as_float(va.y);
+            xa[4 * i + 2] = __uint_as_float(va.z); xa[4 * i + 3] = __uint_as_float(va.w);
+            xb[4 * i + 0] = __uint_as_float(vb.x); xb[4 * i + 1] = __uint_as_float(vb.y);
+            xb[4 * i + 2] = __uint_as_float(vb.z); xb[4 * i + 3] = __uint_as_float(vb.w);
         }
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
             SA += xa[i];
             SB += xb[i];
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) xa[i] = xb[i] = 0.f;
     }
 
-    const int64_t unit_off = (int64_t)b * kBlockBytes;
-    for (int64_t s0 = row_begin; s0 < row_end; s0 += (int64_t)P * RPS) {
-        uint32_t nq[P][NMAT][8];
-        uint4 hd[P][NMAT];
+    int kb = 0, bank = 0;
+    for (int64_t s = s_begin; s < s_end; s += D + 1) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int64_t row = s0 + p * RPS + r;
-            const bool ok = uact && row < row_end;
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                if (ok) {
-                    const uint8_t *base = (m == 0 ? a.W0 : a.W1) + row * rowbytes + unit_off;
-                    hd[p][m] = *reinterpret_cast<const uint4 *>(base);
-                    const uint4 q0 = *reinterpret_cast<const uint4 *>(base + 16 + 32 * g);
-                    const uint4 q1 = *reinterpret_cast<const uint4 *>(base + 32 + 32 * g);
-                    nq[p][m][0] = q0.x; nq[p][m][1] = q0.y; nq[p][m][2] = q0.z; nq[p][m][3] = q0.w;
-                    nq[p][m][4] = q1.x; nq[p][m][5] = q1.y; nq[p][m][6] = q1.z; nq[p][m][7] = q1.w;
-                } else {
-                    hd[p][m] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) nq[p][m][i] = 0u;
-                }
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            if (s0 + p * RPS >= row_end) break;  // uniform: empty batch slot
+        for (int j = 0; j <= D; ++j) {
+            const int64_t sj = s + j;
+            if (sj >= s_end) break;  // uniform
+            // the next sweep's loads go out before this sweep is computed;
+            // past the end they read zeros (unused)
+            if (D > 0) load_slot<NMAT>(buf[(j + D) % (D + 1)], rs, slot_off(sj + D), qoff);
+            if (D == 0) load_slot<NMAT>(buf[0], rs, slot_off(sj), qoff);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                float v = unit_dot(nq[p][m], hd[p][m], xa, xb, SA, SB, sh, upper);
+                float v = unit_dot(buf[j].q[m], buf[j].h[m], xa, xb, SA, SB, sh, upper);
 #pragma unroll
                 for (int off = RPS; off < 64; off <<= 1) v += __shfl_xor(v, off);
-                if (lane < RPS) red[wave][(p * NMAT + m) * RPS + lane] = v;
+                if (lane < RPS) red[bank][wave][(kb * NMAT + m) * RPS + lane] = v;
+            }
+            ++kb;
+            if (kb == FB || sj == s_end - 1) {
+                __syncthreads();
+                if (t < kb * RPS) {
+                    const int k = t / RPS, rr = t % RPS;
+                    const int64_t row = (sj - kb + 1 + k) * RPS + rr;
+                    if (row < row_stop) {
+                        float v0 = 0.f, v1 = 0.f;
+                        for (int w = 0; w < nwaves; ++w) {
+                            v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
+                            if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
+                        }
+                        if (EPI == EPI_STORE) {
+                            if (row < a.split0)
+                                a.o0[row] = v0;
+                            else if (row < a.split1)
+                                a.o1[row - a.split0] = v0;
+                            else
+                                a.o2[row - a.split1] = v0;
+                        } else if (EPI == EPI_GATE_UP) {
+                            a.o0[row] = act_apply(v0, a.act) * v1;
+                        } else {
+                            a.o0[row] = v0;
+                            lg[row - row_begin] = v0;
+                            taken[row - row_begin] = 0;
+                        }
+                    }
+                }
+                kb = 0;
+                bank ^= 1;
             }
         }
-        __syncthreads();
-        if (t < P * RPS) {
-            const int p = t / RPS, rr = t % RPS;
-            const int64_t row = s0 + p * RPS + rr;
-            if (row < row_end) {
-                float v0 = 0.f, v1 = 0.f;
-                for (int w = 0; w < nwaves; ++w) {
-                    v0 += red[w][(p * NMAT + 0) * RPS + rr];
-                    if (NMAT == 2) v1 += red[w][(p * NMAT + 1) * RPS + rr];
-                }
-                if (EPI == EPI_STORE) {
-                    if (row < a.split0)
-                        a.o0[row] = v0;
-                    else if (row < a.split1)
-                        a.o1[row - a.split0] = v0;
-                    else
-                        a.o2[row - a.split1] = v0;
-                } else if (EPI == EPI_GATE_UP) {
-                    a.o0[row] = act_apply(v0, a.act) * v1;
-                } else {
-                    a.o0[row] = v0;
-                    lg[row - row_begin] = v0;
-                    taken[row - row_begin] = 0;
-                }
-            }
-        }
-        __syncthreads();
     }
 
     if (EPI == EPI_LOGITS) {
-        // Per-workgroup top-k of rows [row_begin, row_end): k rounds of a
-        // workgroup-wide max over orderable keys; the winner is removed.
-        const int n = (int)(row_end - row_begin);
+        // Per-workgroup top-k of its rows, written in rank order: k rounds of
+        // a workgroup-wide max over orderable keys; the winner is removed.
+        __syncthreads();
+        const int n = (int)(row_stop - row_begin);
         uint64_t *out = a.cand + (int64_t)blockIdx.x * a.k;
         for (int round = 0; round < a.k; ++round) {
             uint64_t best = 0;
@@ -283,32 +360,41 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     }
 }
 
-// Single-workgroup merge of nc candidate keys into the global top-k.
-constexpr int kMergeThreads = 1024;
-constexpr int kMergePerThread = kMergeCandMax / kMergeThreads;
+// Merge of the per-workgroup candidate lists (each sorted in rank order) into
+// the global top-k: a k-way merge. Thread t owns lists t, t+256, ...; each
+// round the workgroup takes the largest list head and that list advances.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeListsPerThread = 4;   // up to 1024 lists
 
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_t *cand, int nc,
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_t *cand, int nlists,
                                                                     int k, const float *logits,
                                                                     int32_t *top_idx,
                                                                     float *top_val)
 {
     __shared__ uint64_t scratch[kMergeThreads / 64];
     const int t = threadIdx.x;
-    uint64_t mine[kMergePerThread];
+    int pos[kMergeListsPerThread];
+    uint64_t head[kMergeListsPerThread];
 #pragma unroll
-    for (int i = 0; i < kMergePerThread; ++i) {
-        const int c = t + i * kMergeThreads;
-        mine[i] = c < nc ? cand[c] : 0ull;
+    for (int i = 0; i < kMergeListsPerThread; ++i) {
+        const int l = t + i * kMergeThreads;
+        pos[i] = 0;
+        head[i] = l < nlists ? cand[(int64_t)l * k] : 0ull;
     }
     for (int round = 0; round < k; ++round) {
         uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < kMergePerThread; ++i) best = mine[i] > best ? mine[i] : best;
+        for (int i = 0; i < kMergeListsPerThread; ++i) best = head[i] > best ? head[i] : best;
         const uint64_t win = block_max_u64(best, scratch);
         if (win != 0) {
 #pragma unroll
-            for (int i = 0; i < kMergePerThread; ++i)
-                if (mine[i] == win) mine[i] = 0ull;
+            for (int i = 0; i < kMergeListsPerThread; ++i) {
+                if (head[i] == win) {  // keys are unique (they embed the row)
+                    const int l = t + i * kMergeThreads;
+                    ++pos[i];
+                    head[i] = pos[i] < k ? cand[(int64_t)l * k + pos[i]] : 0ull;
+                }
+            }
         }
         if (t == 0) {
             if (win == 0) {
@@ -339,18 +425,44 @@ Shape pick_shape(int64_t cols)
     return {rps, threads};
 }
 
-template <int P, int NMAT, int EPI>
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Workgroups of `threads` threads resident per CU for a kernel using ~vgprs
+// registers per lane (512 per SIMD lane, 4 SIMDs, wave64).
+int wgs_per_cu(int threads, int vgprs)
+{
+    const int waves_per_simd = 512 / vgprs;
+    const int waves = (threads + 63) / 64;
+    const int per_cu = (4 * waves_per_simd) / waves;
+    return per_cu < 1 ? 1 : per_cu;
+}
+
+template <int NMAT, int EPI, int D>
 hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s)
 {
     const dim3 grid((unsigned)nwg), block((unsigned)threads);
     if (threads > 512) {
         // only reachable with one row per sweep (cols > 32768)
-        hipLaunchKernelGGL((rows_kernel<1, 1, NMAT, EPI, 1024>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, 1024, 0>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     switch (rps) {
 #define Q4K_RPS_CASE(R) \
-    case R: hipLaunchKernelGGL((rows_kernel<R, P, NMAT, EPI, 512>), grid, block, 0, s, a); break;
+    case R: hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, 512, D>), grid, block, 0, s, a); break;
         Q4K_RPS_CASE(1)
         Q4K_RPS_CASE(2)
         Q4K_RPS_CASE(4)
@@ -375,15 +487,22 @@ RowsArgs base_args(int64_t rows, int64_t cols)
     return a;
 }
 
-// Rows per workgroup: whole sweeps of rps rows, aiming at about target
-// workgroups.
-int64_t rows_per_wg_for(int64_t rows, int rps, int64_t target_wgs)
+// Persistent grid: as many workgroups as fit on the device at once, never
+// more than there are sweeps, and enough that one workgroup's rows span less
+// than 2^30 bytes (its buffer resource uses 32-bit offsets).
+int64_t grid_for(int64_t rows, int64_t cols, const Shape &sh, int vgprs)
 {
-    int64_t per = (rows + target_wgs - 1) / target_wgs;
-    per = (per + rps - 1) / rps * rps;
-    if (per < rps) per = rps;
-    return per;
+    const int64_t S = (rows + sh.rps - 1) / sh.rps;
+    int64_t g = (int64_t)device_cus() * wgs_per_cu(sh.threads, vgprs);
+    const int64_t sweep_bytes = (int64_t)sh.rps * (cols / kQK) * kBlockBytes;
+    const int64_t max_sweeps = ((int64_t)1 << 30) / sweep_bytes;   // >= 1 for cols <= 65536
+    const int64_t min_g = (S + max_sweeps - 2) / (max_sweeps - 1 > 0 ? max_sweeps - 1 : 1);
+    if (g < min_g) g = min_g;
+    return S < g ? S : g;
 }
+
+constexpr int kVgprStore = 168;   // budget the kernels are written to (3 waves/SIMD)
+constexpr int kLmheadWgs = 512;   // device-independent: fixes the workspace size
 
 }  // namespace
 
@@ -391,7 +510,6 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
                              int64_t rows, int64_t cols, int64_t split0, int64_t split1,
                              hipStream_t s)
 {
-    constexpr int P = 4;
     RowsArgs a = base_args(rows, cols);
     a.W0 = W;
     a.x = x;
@@ -401,15 +519,12 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     a.split0 = split0;
     a.split1 = split1;
     const Shape sh = pick_shape(cols);
-    a.rows_per_wg = rows_per_wg_for(rows, sh.rps, 1024);
-    const int64_t nwg = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
-    return launch_rows<P, 1, EPI_STORE>(a, sh.rps, sh.threads, nwg, s);
+    return launch_rows<1, EPI_STORE, 3>(a, sh.rps, sh.threads, grid_for(rows, cols, sh, kVgprStore), s);
 }
 
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
                           int64_t rows, int64_t cols, int act, hipStream_t s)
 {
-    constexpr int P = 2;
     RowsArgs a = base_args(rows, cols);
     a.W0 = Wg;
     a.W1 = Wu;
@@ -417,24 +532,25 @@ hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, 
     a.o0 = h;
     a.act = act;
     const Shape sh = pick_shape(cols);
-    a.rows_per_wg = rows_per_wg_for(rows, sh.rps, 1024);
-    const int64_t nwg = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
-    return launch_rows<P, 2, EPI_GATE_UP>(a, sh.rps, sh.threads, nwg, s);
+    return launch_rows<2, EPI_GATE_UP, 1>(a, sh.rps, sh.threads, grid_for(rows, cols, sh, kVgprStore),
+                                          s);
 }
 
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols)
 {
     const Shape sh = pick_shape(cols);
-    int64_t per = rows_per_wg_for(rows, sh.rps, 512);
-    if (per > kLmheadRowsPerWgMax) per = kLmheadRowsPerWgMax;
-    return (rows + per - 1) / per;
+    const int64_t S = (rows + sh.rps - 1) / sh.rps;
+    // enough workgroups that each holds at most kLmheadRowsPerWgMax rows
+    int64_t g = kLmheadWgs;
+    const int64_t min_g = (S * sh.rps + kLmheadRowsPerWgMax - 1) / (kLmheadRowsPerWgMax - sh.rps);
+    if (g < min_g) g = min_g;
+    return S < g ? S : g;
 }
 
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,
                               int64_t cols, int k, uint64_t *cand, int32_t *top_idx,
                               float *top_val, hipStream_t s)
 {
-    constexpr int P = 4;
     RowsArgs a = base_args(rows, cols);
     a.W0 = W;
     a.x = x;
@@ -442,14 +558,11 @@ hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, i
     a.cand = cand;
     a.k = k;
     const Shape sh = pick_shape(cols);
-    int64_t per = rows_per_wg_for(rows, sh.rps, 512);
-    if (per > kLmheadRowsPerWgMax) per = kLmheadRowsPerWgMax;
-    a.rows_per_wg = per;
-    const int64_t nwg = (rows + per - 1) / per;
-    hipError_t e = launch_rows<P, 1, EPI_LOGITS>(a, sh.rps, sh.threads, nwg, s);
+    const int64_t nwg = lmhead_num_wgs(rows, cols);
+    hipError_t e = launch_rows<1, EPI_LOGITS, 3>(a, sh.rps, sh.threads, nwg, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeThreads), 0, s, cand,
-                       (int)(nwg * k), k, logits, top_idx, top_val);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeThreads), 0, s, cand, (int)nwg, k,
+                       logits, top_idx, top_val);
     return hipGetLastError();
 }
 

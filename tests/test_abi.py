@@ -117,7 +117,7 @@ def test_lmhead_validation():
     assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, D + 8, F, need, S) == q4k.Q4K_ERR_ALIAS
     assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, E, C + 64, need, S) == q4k.Q4K_ERR_ALIAS
     # a vocabulary too large for the single-workgroup merge at k = 64
-    assert L.q4k_lmhead_topk(A, B, C, 4_000_000, 256, 64, D, E, F, 1 << 40, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_lmhead_topk(A, B, C, 5_000_000, 256, 64, D, E, F, 1 << 40, S) == q4k.Q4K_ERR_SHAPE
 
 
 def test_prefill_validation():

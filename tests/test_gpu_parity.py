@@ -355,3 +355,50 @@ def test_errors_raise_and_enqueue_nothing(q4k):
         q4k.q4k_matvec(W, x, W, 10, 256)          # output aliases W
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+def test_graph_replays_match_eager(q4k):
+    """A decode step captured in a HIP graph and replayed several times, with
+    eager launches and synchronisations in between, reproduces the eager
+    result bit for bit on every replay."""
+    rng = np.random.default_rng(51)
+    hidden, inter, qr, kr, vocab = 512, 1280, 256, 128, 5000
+    Wqkv = dev(inputs.q4k_random(rng, qr + 2 * kr, hidden))
+    Wg = dev(inputs.q4k_random(rng, inter, hidden))
+    Wu = dev(inputs.q4k_random(rng, inter, hidden))
+    Wd = dev(inputs.q4k_random(rng, hidden, inter))
+    Wl = dev(inputs.q4k_random(rng, vocab, hidden))
+    x = dev(inputs.normal_f32(rng, hidden))
+    q, k, v = (torch.empty(n, device="cuda") for n in (qr, kr, kr))
+    y = torch.empty(hidden, device="cuda")
+    ws = q4k.workspace(q4k.q4k_ffn_workspace_bytes(hidden, inter))
+    logits = torch.empty(vocab, device="cuda")
+    ti = torch.empty(5, dtype=torch.int32, device="cuda")
+    tv = torch.empty(5, device="cuda")
+    wl = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(vocab, hidden, 5))
+
+    def step():
+        q4k.q4k_qkv(Wqkv, x, q, k, v, qr, kr, hidden)
+        q4k.q4k_ffn(Wg, Wu, Wd, x, y, hidden, inter, 0, ws)
+        q4k.q4k_lmhead_topk(Wl, x, logits, vocab, hidden, 5, ti, tv, wl)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (q, k, v, y, logits, ti, tv)]
+
+    step()
+    ref = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for it in range(4):
+        for t in (q, k, v, y, logits, tv):
+            t.fill_(float("nan"))
+        ti.fill_(-7)
+        g.replay()
+        got = snapshot()
+        for a, b in zip(ref, got):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), it
+        step()                      # eager work between replays
+        torch.cuda.synchronize()
