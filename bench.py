@@ -107,7 +107,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--kernel-only", default="", help="launch only this part (profiling): "
-                    "gate_up | down | qkv | lmhead")
+                    "gate_up | down | qkv | lmhead | copy (a plain 1 GiB device copy that "
+                    "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -136,7 +137,8 @@ def main() -> int:
     # ---------------------------------------------------------------- inputs
     t0 = time.perf_counter()
     qkv_host, ffn_host, qkv_dev, ffn_dev = [], [], [], []
-    for l in range(LAYERS):
+    need_layers = args.kernel_only in ("", "gate_up", "down", "qkv")
+    for l in range(LAYERS if need_layers else 0):
         c = inputs.qkv(copy=l)
         L = inputs.ffn_layer(l)
         qkv_dev.append({"W": up(c["W"]), "x": up(c["x"])})
@@ -146,8 +148,9 @@ def main() -> int:
             ffn_host.append(L)
         if l % 8 == 7:
             log(f"generated {l + 1}/{LAYERS} layers ({time.perf_counter() - t0:.1f}s)")
-    lm = inputs.lm_head()
-    lm_dev = {"W": up(lm["W"]), "x": up(lm["x"])}
+    need_lm = args.kernel_only in ("", "lmhead")
+    lm = inputs.lm_head() if need_lm else None
+    lm_dev = {"W": up(lm["W"]), "x": up(lm["x"])} if need_lm else None
     torch.cuda.synchronize()
     log(f"inputs resident: {(LAYERS * (QKV_BYTES + GATE_UP_BYTES + DOWN_BYTES) + LMHEAD_BYTES) / 1e9:.2f} GB "
         f"({time.perf_counter() - t0:.1f}s)")
@@ -173,6 +176,14 @@ def main() -> int:
         q4k.q4k_lmhead_topk(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx, top_val,
                             lm_ws)
 
+    if args.kernel_only == "copy":
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for i in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"kernel-only copy: {args.warmup + args.steps} copies of 1 GiB done")
+        return 0
     if args.kernel_only:
         # profiling helper: launch one kind of kernel over the 34 layers
         parts = {
@@ -245,18 +256,25 @@ def main() -> int:
     eager_ms = (time.perf_counter() - te) * 1e3 / n_eager
 
     # ------------------------------------- dominant kernel: fused gate+up
-    reps = 5
-    per_launch = []
-    for _ in range(reps):
-        pairs = []
+    # 34 back-to-back launches (one per layer, so every launch streams its
+    # weights from HBM) captured in a graph; the per-launch average from HIP
+    # events on the replay stream is the kernel's duration (graph replay
+    # leaves no gaps between the kernels).
+    g_gu = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_gu):
         for L in ffn_dev:
-            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_ev.record(stream)
             q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], h, INTER, HIDDEN, GELU)
-            b_ev.record(stream)
-            pairs.append((a_ev, b_ev))
+    torch.cuda.synchronize()
+    g_gu.replay()
+    torch.cuda.synchronize()
+    per_launch = []
+    for _ in range(5):
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        g_gu.replay()
+        b_ev.record(stream)
         torch.cuda.synchronize()
-        per_launch.append(sum(a.elapsed_time(b) for a, b in pairs) / len(pairs))
+        per_launch.append(a_ev.elapsed_time(b_ev) / len(ffn_dev))
     per_launch.sort()
     gu_ms = per_launch[len(per_launch) // 2]
     gu_gbs = GATE_UP_BYTES / (gu_ms * 1e-3) / 1e9

@@ -102,13 +102,13 @@ int q4k_qkv(const void *Wqkv, const float *x, float *q, float *k, float *v,
 int q4k_gate_up(const void *Wg, const void *Wu, const float *x, float *h,
                 int64_t inter, int64_t hidden, int act, void *stream);
 
-/* Workspace of q4k_ffn: h, f32[inter] (16-byte aligned). */
+/* Workspace of q4k_ffn: the intermediate h, f32[inter] (16-byte aligned). */
 size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter);
 
 /* Gated FFN for one token: h = act(Wg x) * (Wu x) (q4k_gate_up), then
  * y = Wd h (Wd: hidden x inter). x: f32[hidden]; y: f32[hidden]; h lives in
- * ws. Source: infer-compute README, "Shaders" table (q4k_ffn_gate_up followed
- * by q4k_geglu_gelu_tanh_down / q4k_geglu_silu_down). */
+ * ws. Source: infer-compute README, "Shaders" table (q4k_ffn_gate_up
+ * followed by q4k_geglu_gelu_tanh_down / q4k_geglu_silu_down). */
 int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
             int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes, void *stream);
 

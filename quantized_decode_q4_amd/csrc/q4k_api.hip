@@ -140,20 +140,15 @@ Q4K_EXPORT int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const flo
     if (overlap(sy, sw)) return Q4K_ERR_ALIAS;
     for (int j = 0; j < 4; ++j)
         if (overlap(sy, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
-    float *h = (float *)ws;
-    hipStream_t s = as_stream(stream);
-    int st = hip_status(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu, x, h, inter,
-                                            hidden, act, s));
-    if (st != Q4K_OK) return st;
-    return hip_status(
-        q4k::launch_rows_store((const uint8_t *)Wd, h, y, nullptr, nullptr, hidden, inter, hidden,
-                               hidden, s));
+    return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                      (const uint8_t *)Wd, x, y, hidden, inter, act,
+                                      (float *)ws, as_stream(stream)));
 }
 
 Q4K_EXPORT size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k)
 {
     if (!rows_ok(rows) || !cols_ok(cols) || rows == 0 || k < 1 || k > Q4K_TOPK_MAX) return 0;
-    return round_up((size_t)q4k::lmhead_num_wgs(rows, cols) * (size_t)k * 8, 256);
+    return round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * (size_t)k * 8, 256);
 }
 
 Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int64_t rows,
@@ -162,8 +157,7 @@ Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int
 {
     if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
     if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
-    const int64_t nwg = q4k::lmhead_num_wgs(rows, cols);
-    if (nwg > q4k::kMergeListsMax) return Q4K_ERR_SHAPE;
+    if (q4k::lmhead_max_wgs(rows, cols) > q4k::kMergeListsMax) return Q4K_ERR_SHAPE;
     if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||
         !aligned(top_val, 4))
@@ -250,13 +244,11 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
     for (int j = 0; j < 4; ++j)
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
-    float *h = (float *)ws;
     for (int64_t t = 0; t < seq; ++t) {
-        int st = hip_status(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu,
-                                                X + t * hidden, h, inter, hidden, act, s));
-        if (st != Q4K_OK) return st;
-        st = hip_status(q4k::launch_rows_store((const uint8_t *)Wd, h, Y + t * hidden, nullptr,
-                                               nullptr, hidden, inter, hidden, hidden, s));
+        const int st = hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                                  (const uint8_t *)Wd, X + t * hidden,
+                                                  Y + t * hidden, hidden, inter, act,
+                                                  (float *)ws, s));
         if (st != Q4K_OK) return st;
     }
     return Q4K_OK;

@@ -14,6 +14,11 @@ constexpr int kColsMax = 65536;
 constexpr int kLmheadRowsPerWgMax = 4096;
 constexpr int kMergeListsMax = 1024;    // per-workgroup candidate lists the merge takes
 
+// Block-floating-point activation planes of n activations (n a multiple of
+// 256) as staged in LDS: three byte planes of n bytes, then n/32 scales and
+// n/32 sums (f32).
+__host__ __device__ constexpr int64_t planes_bytes(int64_t n) { return 3 * n + n / 4; }
+
 // Row-streaming kernels (q4k_rows.hip).
 // y rows [0, split0) -> o0, [split0, split1) -> o1, [split1, rows) -> o2.
 hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float *o1, float *o2,
@@ -21,8 +26,14 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
                              hipStream_t s);
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
                           int64_t rows, int64_t cols, int act, hipStream_t s);
-// lm_head: number of candidate-producing workgroups for a shape (device independent).
+// Gated FFN: gate+up with the activation applied (h, f32[inter]), then the
+// down projection reading h.
+hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
+                      float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s);
+// lm_head: candidate-producing workgroups used on this device, and the most
+// any device uses for the shape (sizes the workspace).
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols);
+int64_t lmhead_max_wgs(int64_t rows, int64_t cols);
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,
                               int64_t cols, int k, uint64_t *cand, int32_t *top_idx,
                               float *top_val, hipStream_t s);

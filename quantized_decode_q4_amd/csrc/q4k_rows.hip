@@ -1,6 +1,6 @@
 // Row-streaming Q4_K kernels for decode (one activation vector):
 //   matvec / fused QKV, fused gate+up with the gated activation, and the
-//   lm_head matvec with a per-workgroup top-k plus a single-workgroup merge.
+//   lm_head matvec with a per-workgroup top-k plus a k-way merge.
 //
 // Sources: infer-compute README, "Shaders" table (q4k_matvec, q4k_qkv_proj,
 // q4k_ffn_gate_up, geglu_gelu_tanh / geglu_silu) and "Key Optimizations"
@@ -12,32 +12,80 @@
 //  * A row of cols = 256*nb weights is nb super-blocks. Each block splits into
 //    four 32-byte "units": unit g holds quant bytes 32g..32g+31, i.e. all 32
 //    weights of sub-block 2g (low nibbles) and of sub-block 2g+1 (high
-//    nibbles). A row has U = 4*nb units.
+//    nibbles). A row has U = 4*nb units; unit u covers columns 64u..64u+63.
 //  * Thread t of a workgroup owns unit u = t / RPS of rows r = t % RPS of every
-//    sweep: the workgroup covers RPS consecutive rows per sweep and walks its
-//    contiguous row range. The thread keeps the 64 activations of its unit in
-//    registers for the whole kernel (loaded once, reused for every row), so
-//    the activation is read from memory once per thread, not once per row.
-//  * Per row the thread loads 2 x 16 B of quants and the 16 B block header
-//    (d, dmin, packed 6-bit scales/mins) with 128-bit loads; a wave covers
-//    64/RPS consecutive units of RPS rows, so each load instruction reads
-//    contiguous runs of every row.
+//    sweep (RPS consecutive rows). The workgroup walks a contiguous range of
+//    sweeps (a persistent grid), keeping D sweeps of loads in flight while it
+//    computes one (a register ring). The thread's activations stay in
+//    registers for the whole kernel.
+//  * Per row the thread reads 2 x 16 B of quants and the 16 B block header
+//    with unconditional bounds-checked buffer loads.
 //  * Partial dot products are reduced across the 64/RPS units of a wave with
 //    xor shuffles, then across waves through LDS, in a fixed order (results
 //    are deterministic; no atomics).
-//  * Dequantisation uses w = d*sc*q - dmin*m per 32-weight sub-block s:
-//      sum_j w_j x_j = d*sc_s*sum_j q_j x_j - dmin*m_s*sum_j x_j,
-//    so the min term needs only the per-thread activation sums.
+//
+// Arithmetic. w = d*sc_s*q - dmin*m_s per 32-weight sub-block s, so
+//     sum_j w_j x_j = d*sc_s*sum_j q_j x_j - dmin*m_s*sum_j x_j.
+// The activations of each sub-block are held in block floating point:
+//     x_j = X_s * (p0_j + 256 p1_j + 65536 p2_j),  X_s = 2^(e_s - 22),
+// with max_j |x_j| < 2^e_s, p0, p1 unsigned bytes and p2 a signed byte (the
+// two's-complement bytes of a 24-bit integer |x_int| <= 2^22; rounding error
+// <= 2^-23 of the sub-block maximum, the resolution of f32 at that maximum).
+// sum_j q_j x_j is then three byte dot products (v_dot4_u32_u8 for p0, p1,
+// v_dot4_i32_i8 for p2) on the raw nibbles, exact in 32-bit integers, scaled
+// by X_s once per sub-block. The min term uses the f32 sum of the sub-block's
+// activations. Non-finite activations make X_s NaN (outputs become NaN).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "q4k_internal.h"
 
+// Launch tunables, chosen by timing sweeps on MI355X (1, 2, 3, 4, 8
+// workgroups per CU; 0 to 3 sweeps in flight): one persistent workgroup per
+// CU and one sweep in flight were best or within 2% of best for every shape
+// of the decode step.
+#ifndef Q4K_ROWS_FB
+#define Q4K_ROWS_FB 8               // sweeps per cross-wave reduction batch
+#endif
+#ifndef Q4K_STORE_D
+#define Q4K_STORE_D 1               // sweeps in flight, matvec / QKV
+#endif
+#ifndef Q4K_STORE_WGS_PER_CU
+#define Q4K_STORE_WGS_PER_CU 1
+#endif
+#ifndef Q4K_GATE_UP_D
+#define Q4K_GATE_UP_D 1
+#endif
+#ifndef Q4K_GATE_UP_WGS_PER_CU
+#define Q4K_GATE_UP_WGS_PER_CU 1
+#endif
+#ifndef Q4K_DOWN_D
+#define Q4K_DOWN_D 1
+#endif
+#ifndef Q4K_DOWN_WGS_PER_CU
+#define Q4K_DOWN_WGS_PER_CU 1
+#endif
+#ifndef Q4K_LMHEAD_D
+#define Q4K_LMHEAD_D 1
+#endif
+#ifndef Q4K_LMHEAD_WGS_PER_CU
+#define Q4K_LMHEAD_WGS_PER_CU 2
+#endif
+
 namespace q4k {
 namespace {
 
-enum Epi { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_LOGITS = 2 };
+enum Epi { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_LOGITS = 3 };
+// How the thread holds its 64 activations:
+//  XS_LDS    block floating point, converted cooperatively by the workgroup
+//            through LDS (byte dot products)
+//  XS_THREAD block floating point, each thread converts its own 64 (rows too
+//            wide for the LDS copy)
+//  XS_F32    plain f32 in registers (f32 multiply-adds). Used where a thread
+//            computes only a few rows, so that no conversion has to be paid
+//            for: the down projection of the FFN.
+enum XSrc { XS_LDS = 0, XS_THREAD = 1, XS_F32 = 3 };
 
 struct RowsArgs {
     const uint8_t *W0;
@@ -46,15 +94,15 @@ struct RowsArgs {
     float *o0;
     float *o1;
     float *o2;
-    uint64_t *cand;
+    uint64_t *cand;          // EPI_LOGITS
     int64_t rows;
     int64_t split0;
     int64_t split1;
-    int64_t rows_per_wg;
     int32_t nb;
     int32_t U;
     int32_t act;
     int32_t k;
+    int32_t chunk;           // sweeps per unit of the workgroup split
 };
 
 __device__ __forceinline__ float act_apply(float z, int act)
@@ -66,100 +114,7 @@ __device__ __forceinline__ float act_apply(float z, int act)
     return z / (1.0f + expf(-z));
 }
 
-// Partial dot product of one unit (sub-blocks A = 2g and B = 2g+1 of a block)
-// of one row with the thread's 64 activations.
-//   nq[0..7]: the 32 quant bytes; hd: the 16-byte block header.
-// Low nibbles are A's quants; high nibbles are kept in place (16*q) and the
-// factor 1/16 is folded into B's scale (exact, a power of two).
-__device__ __forceinline__ uint32_t and_opaque(uint32_t v, uint32_t m)
-{
-    // An AND the optimiser cannot see through: the byte conversions below then
-    // stay single v_cvt_f32_ubyte{0..3} instructions instead of a bit-field
-    // extract followed by a conversion.
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(m), "v"(v));
-    return r;
-}
-
-__device__ __forceinline__ float unit_dot(const uint32_t (&nq)[8], uint4 hd,
-                                          const float (&xa)[32], const float (&xb)[32],
-                                          float SA, float SB, int sh, bool upper)
-{
-    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t lo = and_opaque(nq[k], 0x0F0F0F0Fu);
-        const uint32_t hi = and_opaque(nq[k], 0xF0F0F0F0u);
-        a0 = fmaf((float)(lo & 0xFFu), xa[4 * k + 0], a0);
-        a1 = fmaf((float)((lo >> 8) & 0xFFu), xa[4 * k + 1], a1);
-        a0 = fmaf((float)((lo >> 16) & 0xFFu), xa[4 * k + 2], a0);
-        a1 = fmaf((float)(lo >> 24), xa[4 * k + 3], a1);
-        b0 = fmaf((float)(hi & 0xFFu), xb[4 * k + 0], b0);
-        b1 = fmaf((float)((hi >> 8) & 0xFFu), xb[4 * k + 1], b1);
-        b0 = fmaf((float)((hi >> 16) & 0xFFu), xb[4 * k + 2], b0);
-        b1 = fmaf((float)(hi >> 24), xb[4 * k + 3], b1);
-    }
-    const float d = __half2float(__ushort_as_half((unsigned short)(hd.x & 0xFFFFu)));
-    const float dmin = __half2float(__ushort_as_half((unsigned short)(hd.x >> 16)));
-    // Scale bytes: hd.y = s[0..3], hd.z = s[4..7], hd.w = s[8..11].
-    // Sub-blocks 0..3: sc = s[j] & 63, m = s[j+4] & 63.
-    // Sub-blocks 4..7: sc = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
-    //                  m  = (s[j+4] >> 4) | (s[j]   >> 6) << 4.
-    // This unit needs the byte pair starting at 2*(g&1) (shift sh = 16*(g&1)).
-    const uint32_t sc_src = upper ? hd.w : hd.y;
-    const uint32_t m_src = upper ? (hd.w >> 4) : hd.z;
-    const uint32_t low_mask = upper ? 0x0F0Fu : 0x3F3Fu;
-    const uint32_t top_mask = upper ? 0x3030u : 0u;
-    const uint32_t sc2 = ((sc_src >> sh) & low_mask) | ((hd.y >> (sh + 2)) & top_mask);
-    const uint32_t m2 = ((m_src >> sh) & low_mask) | ((hd.z >> (sh + 2)) & top_mask);
-    const float scA = (float)(sc2 & 0xFFu);
-    const float scB = (float)((sc2 >> 8) & 0xFFu) * 0.0625f;
-    const float mA = (float)(m2 & 0xFFu);
-    const float mB = (float)((m2 >> 8) & 0xFFu);
-    const float t1 = fmaf(scA, a0 + a1, scB * (b0 + b1));
-    const float t2 = fmaf(mA, SA, mB * SB);
-    return fmaf(d, t1, -dmin * t2);
-}
-
-// Orderable 64-bit key of a (logit, row) pair: larger key = earlier in the
-// top-k order (value descending, then index ascending). NaN maps to the
-// lowest value class (high word 0); key 0 itself means "no candidate".
-__device__ __forceinline__ uint64_t topk_key(float v, uint32_t idx)
-{
-    uint32_t hi;
-    if (v != v) {
-        hi = 0u;
-    } else {
-        if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
-        const uint32_t b = __float_as_uint(v);
-        hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    }
-    return ((uint64_t)hi << 32) | (uint64_t)(~idx);
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off)
-{
-    const uint32_t lo = __shfl_xor((unsigned int)(v & 0xFFFFFFFFu), off);
-    const uint32_t hi = __shfl_xor((unsigned int)(v >> 32), off);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Workgroup-wide maximum of a 64-bit key (all threads get the result).
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
-{
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t o = shfl_xor_u64(v, off);
-        v = o > v ? o : v;
-    }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nwaves = (blockDim.x + 63) >> 6;
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    uint64_t m = 0;
-    for (int w = 0; w < nwaves; ++w) m = scratch[w] > m ? scratch[w] : m;
-    __syncthreads();
-    return m;
-}
+// ---------------------------------------------------------------- loads ---
 
 // Unconditional 16-byte loads through a bounds-checked buffer resource: an
 // offset at or beyond the resource's size reads zeros instead of faulting, so
@@ -204,37 +159,279 @@ __device__ __forceinline__ void load_slot(Slot<NMAT> &sl, const __amdgpu_buffer_
     }
 }
 
+// ------------------------------------------------ block floating point ---
+
+// Shift taking the sub-block to 22-bit integers and the scale back; the
+// maximum magnitude amax and the f32 sum (NaN/Inf detector) are given.
+__device__ __forceinline__ void bfp_params(float amax, float sum, int &shift, float &X)
+{
+    const int e = __builtin_amdgcn_frexp_expf(amax);   // amax < 2^e
+    shift = 22 - e;
+    X = __builtin_amdgcn_ldexpf(1.0f, e - 22);
+    if (amax == 0.0f) {
+        shift = 0;
+        X = 0.0f;
+    }
+    if (!(fabsf(sum) <= 3.402823466e38f) || !(amax <= 3.402823466e38f))
+        X = __int_as_float(0x7FC00000);
+}
+
+__device__ __forceinline__ int to_int22(float v, int shift)
+{
+    return (int)__builtin_rintf(__builtin_amdgcn_ldexpf(v, shift));
+}
+
+// Bytes 0, 1, 2 of four 24-bit integers a, b, c, d, transposed into plane
+// dwords: P0 = [a.b0 b.b0 c.b0 d.b0], P1 = [.. b1 ..], P2 = [.. b2 ..].
+__device__ __forceinline__ void pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                      uint32_t &P0, uint32_t &P1, uint32_t &P2)
+{
+    const uint32_t u01 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t u23 = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+    P0 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+    P1 = __builtin_amdgcn_perm(u23, u01, 0x07060302u);
+    P2 = __builtin_amdgcn_perm(b, a, 0x0c0c0602u) | __builtin_amdgcn_perm(d, c, 0x06020c0cu);
+}
+
+// The thread's 64 activations (sub-blocks A = 2u and B = 2u+1) as planes.
+struct XUnit {
+    uint32_t pa[3][8];
+    uint32_t pb[3][8];
+    float XA, XB, SA, SB;
+};
+
+// Convert 32 f32 activations into planes (per-thread path).
+__device__ __forceinline__ void planes32(const float (&v)[32], uint32_t (&p)[3][8], float &X,
+                                         float &S)
+{
+    float amax = 0.f, sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        amax = fmaxf(amax, fabsf(v[i]));
+        sum += v[i];
+    }
+    int shift;
+    bfp_params(amax, sum, shift, X);
+    S = sum;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        pack4((uint32_t)to_int22(v[4 * k], shift), (uint32_t)to_int22(v[4 * k + 1], shift),
+              (uint32_t)to_int22(v[4 * k + 2], shift), (uint32_t)to_int22(v[4 * k + 3], shift),
+              p[0][k], p[1][k], p[2][k]);
+}
+
+// ------------------------------------------------------------ compute ---
+
+// Partial dot product of one unit of one row with the thread's activations.
+__device__ __forceinline__ float unit_dot(const uint32_t (&nq)[8], uint4 hd, const XUnit &xu,
+                                          int sh, bool upper)
+{
+    uint32_t a0 = 0u, a1 = 0u, b0 = 0u, b1 = 0u;
+    int a2 = 0, b2 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t lo = nq[k] & 0x0F0F0F0Fu;          // sub-block A quants
+        const uint32_t hi = (nq[k] >> 4) & 0x0F0F0F0Fu;   // sub-block B quants
+        a0 = __builtin_amdgcn_udot4(lo, xu.pa[0][k], a0, false);
+        a1 = __builtin_amdgcn_udot4(lo, xu.pa[1][k], a1, false);
+        a2 = __builtin_amdgcn_sdot4((int)lo, (int)xu.pa[2][k], a2, false);
+        b0 = __builtin_amdgcn_udot4(hi, xu.pb[0][k], b0, false);
+        b1 = __builtin_amdgcn_udot4(hi, xu.pb[1][k], b1, false);
+        b2 = __builtin_amdgcn_sdot4((int)hi, (int)xu.pb[2][k], b2, false);
+    }
+    // a0 + 256 a1 < 2^25 fits in 32 bits exactly
+    const float gA = fmaf(65536.0f, (float)a2, (float)(a0 + (a1 << 8)));
+    const float gB = fmaf(65536.0f, (float)b2, (float)(b0 + (b1 << 8)));
+
+    const float d = __half2float(__ushort_as_half((unsigned short)(hd.x & 0xFFFFu)));
+    const float dmin = __half2float(__ushort_as_half((unsigned short)(hd.x >> 16)));
+    // Scale bytes: hd.y = s[0..3], hd.z = s[4..7], hd.w = s[8..11].
+    // Sub-blocks 0..3: sc = s[j] & 63, m = s[j+4] & 63.
+    // Sub-blocks 4..7: sc = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+    //                  m  = (s[j+4] >> 4) | (s[j]   >> 6) << 4.
+    // This unit needs the byte pair starting at 2*(g&1) (shift sh = 16*(g&1)).
+    const uint32_t sc_src = upper ? hd.w : hd.y;
+    const uint32_t m_src = upper ? (hd.w >> 4) : hd.z;
+    const uint32_t low_mask = upper ? 0x0F0Fu : 0x3F3Fu;
+    const uint32_t top_mask = upper ? 0x3030u : 0u;
+    const uint32_t sc2 = ((sc_src >> sh) & low_mask) | ((hd.y >> (sh + 2)) & top_mask);
+    const uint32_t m2 = ((m_src >> sh) & low_mask) | ((hd.z >> (sh + 2)) & top_mask);
+    const float scA = (float)(sc2 & 0xFFu);
+    const float scB = (float)((sc2 >> 8) & 0xFFu);
+    const float mA = (float)(m2 & 0xFFu);
+    const float mB = (float)((m2 >> 8) & 0xFFu);
+    const float t1 = fmaf(scA * xu.XA, gA, (scB * xu.XB) * gB);
+    const float t2 = fmaf(mA, xu.SA, mB * xu.SB);
+    return fmaf(d, t1, -dmin * t2);
+}
+
+// An AND the optimiser cannot see through: the byte conversions of the f32
+// path then stay single v_cvt_f32_ubyte{0..3} instructions instead of a
+// bit-field extract followed by a conversion.
+__device__ __forceinline__ uint32_t and_opaque(uint32_t v, uint32_t m)
+{
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(m), "v"(v));
+    return r;
+}
+
+// f32 path: the thread's 64 activations and their sub-block sums.
+struct XF32 {
+    float xa[32], xb[32];
+    float SA, SB;
+};
+
+// Partial dot product of one unit of one row, f32 multiply-adds. Low nibbles
+// are A's quants; high nibbles are kept in place (16q) and the factor 1/16 is
+// folded into B's scale (exact, a power of two).
+__device__ __forceinline__ float unit_dot_f32(const uint32_t (&nq)[8], uint4 hd, const XF32 &xf,
+                                              int sh, bool upper)
+{
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t lo = and_opaque(nq[k], 0x0F0F0F0Fu);
+        const uint32_t hi = and_opaque(nq[k], 0xF0F0F0F0u);
+        a0 = fmaf((float)(lo & 0xFFu), xf.xa[4 * k + 0], a0);
+        a1 = fmaf((float)((lo >> 8) & 0xFFu), xf.xa[4 * k + 1], a1);
+        a0 = fmaf((float)((lo >> 16) & 0xFFu), xf.xa[4 * k + 2], a0);
+        a1 = fmaf((float)(lo >> 24), xf.xa[4 * k + 3], a1);
+        b0 = fmaf((float)(hi & 0xFFu), xf.xb[4 * k + 0], b0);
+        b1 = fmaf((float)((hi >> 8) & 0xFFu), xf.xb[4 * k + 1], b1);
+        b0 = fmaf((float)((hi >> 16) & 0xFFu), xf.xb[4 * k + 2], b0);
+        b1 = fmaf((float)(hi >> 24), xf.xb[4 * k + 3], b1);
+    }
+    const float d = __half2float(__ushort_as_half((unsigned short)(hd.x & 0xFFFFu)));
+    const float dmin = __half2float(__ushort_as_half((unsigned short)(hd.x >> 16)));
+    const uint32_t sc_src = upper ? hd.w : hd.y;
+    const uint32_t m_src = upper ? (hd.w >> 4) : hd.z;
+    const uint32_t low_mask = upper ? 0x0F0Fu : 0x3F3Fu;
+    const uint32_t top_mask = upper ? 0x3030u : 0u;
+    const uint32_t sc2 = ((sc_src >> sh) & low_mask) | ((hd.y >> (sh + 2)) & top_mask);
+    const uint32_t m2 = ((m_src >> sh) & low_mask) | ((hd.z >> (sh + 2)) & top_mask);
+    const float scA = (float)(sc2 & 0xFFu);
+    const float scB = (float)((sc2 >> 8) & 0xFFu) * 0.0625f;
+    const float mA = (float)(m2 & 0xFFu);
+    const float mB = (float)((m2 >> 8) & 0xFFu);
+    const float t1 = fmaf(scA, a0 + a1, scB * (b0 + b1));
+    const float t2 = fmaf(mA, xf.SA, mB * xf.SB);
+    return fmaf(d, t1, -dmin * t2);
+}
+
+// ------------------------------------------------------ wave reduction ---
+
+// Sum over the lanes of a wave that are congruent modulo RPS (every lane gets
+// its class's sum). Within 16-lane rows a cyclic rotation by `off` pairs lane
+// i with i+off (mod 16), which is all a sum needs; across rows the gfx950
+// permlane swaps exchange rows (16) and halves (32): v_permlane32_swap x, y
+// swaps the upper half of x with the lower half of y, so with x = y = v the
+// two registers add up to v + v[lane ^ 32] (likewise for 16-lane rows). No
+// LDS traffic, unlike a shuffle through ds_bpermute.
+// The swaps are written as inline asm: with the builtin, this compiler folds
+// the sum of the two results of a swap of equal inputs into twice the first
+// result (a miscompile found on MI355X; the asm form was checked there
+// against a CPU sum for every RPS).
+template <int RPS>
+__device__ __forceinline__ float wave_sum_mod(float v)
+{
+    if (RPS <= 1) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+    if (RPS <= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
+    if (RPS <= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    if (RPS <= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    if (RPS <= 16) {
+        float x = v, y = v;
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+        v = x + y;
+    }
+    if (RPS <= 32) {
+        float x = v, y = v;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+        v = x + y;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- top-k ---
+
+// Orderable 64-bit key of a (logit, row) pair: larger key = earlier in the
+// top-k order (value descending, then index ascending). NaN maps to the
+// lowest value class (high word 0); key 0 itself means "no candidate".
+__device__ __forceinline__ uint64_t topk_key(float v, uint32_t idx)
+{
+    uint32_t hi;
+    if (v != v) {
+        hi = 0u;
+    } else {
+        if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
+        const uint32_t b = __float_as_uint(v);
+        hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    }
+    return ((uint64_t)hi << 32) | (uint64_t)(~idx);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off)
+{
+    const uint32_t lo = __shfl_xor((unsigned int)(v & 0xFFFFFFFFu), off);
+    const uint32_t hi = __shfl_xor((unsigned int)(v >> 32), off);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Workgroup-wide maximum of a 64-bit key (all threads get the result).
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
+{
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = shfl_xor_u64(v, off);
+        v = o > v ? o : v;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = (blockDim.x + 63) >> 6;
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    uint64_t m = 0;
+    for (int w = 0; w < nwaves; ++w) m = scratch[w] > m ? scratch[w] : m;
+    __syncthreads();
+    return m;
+}
+
+// ----------------------------------------------------------- the kernel ---
+
 // Persistent row-streaming kernel.
 //  RPS  rows per sweep (threads t = u*RPS + r own unit u of row r of a sweep)
 //  NMAT 1 (one matrix) or 2 (gate and up rows sharing the activation)
-//  EPI  epilogue: store / gated activation / logits + block top-k
+//  EPI  epilogue: store (3-way row split) / gated activation / logits + top-k
+//  XS   how the activations are held (see XSrc)
 //  D    sweeps whose loads are in flight while one sweep is computed
-// Workgroup w processes the contiguous sweeps [S*w/G, S*(w+1)/G) of the
-// S = ceil(rows / RPS) sweeps. The quant/header loads of the first D sweeps
-// are issued before the activation slice, then every step issues sweep i+D
-// and computes sweep i (a register ring of D+1 slots, statically indexed by
-// unrolling). Wave partial sums go to an LDS bank; every FB sweeps one barrier
-// publishes them and threads t < FB*RPS finish the rows.
-template <int RPS, int NMAT, int EPI, int MAXT, int D>
+// Workgroup w processes the contiguous sweeps [S*w/G, S*(w+1)/G). The
+// activation loads and the quant/header loads of the first D sweeps are
+// issued first; then every step issues sweep i+D and computes sweep i. Wave
+// partial sums go to an LDS bank; every fb sweeps one barrier publishes them
+// and threads t < fb*RPS finish those rows.
+template <int RPS, int NMAT, int EPI, int XS, int MAXT, int D>
 __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 {
     static_assert(RPS >= 1 && RPS <= 64 && (64 % RPS) == 0, "RPS must divide 64");
     constexpr int NW = MAXT / 64;
-    constexpr int FB = 8;
+    constexpr int FB = Q4K_ROWS_FB;
+    constexpr bool kInt = XS != XS_F32;
     __shared__ float red[2][NW][FB * NMAT * RPS];
     __shared__ float lg[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint8_t taken[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint64_t keys_scratch[EPI == EPI_LOGITS ? NW : 1];
+    extern __shared__ uint4 xlds_v[];   // XS_LDS: planes of x (planes_bytes(cols))
+    uint8_t *const xlds = reinterpret_cast<uint8_t *>(xlds_v);
 
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = blockDim.x >> 6;
+    // sweeps per reduction batch: every row of a batch needs a thread
+    const int fb = min(FB, (int)(blockDim.x / RPS));
     const int u = t / RPS;
     const int r = t % RPS;
     const bool uact = u < a.U;
     const int b = u >> 2, g = u & 3;
     const int sh = (g & 1) * 16;
     const bool upper = g >= 2;
+    const int64_t cols = (int64_t)a.nb * kQK;
     const int64_t rowbytes = (int64_t)a.nb * kBlockBytes;
     const int64_t unit_off = (int64_t)b * kBlockBytes;
     const int64_t S = (a.rows + RPS - 1) / RPS;
@@ -244,96 +441,196 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int64_t row_stop = min(s_end * RPS, a.rows);
 
     // Buffer resources over this workgroup's rows (the host keeps the span
-    // below 2^31 bytes); offsets are relative to row_begin.
+    // below 2^30 bytes); offsets are relative to row_begin.
     __amdgpu_buffer_rsrc_t rs[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
         rs[m] = make_rsrc((m == 0 ? a.W0 : a.W1) + row_begin * rowbytes,
                           (uint32_t)((row_stop - row_begin) * rowbytes));
     const uint32_t qoff = 16u + 32u * (uint32_t)g;
-    // byte offset of (sweep s, this thread's row) or kOutOfRange
     auto slot_off = [&](int64_t sw) -> uint32_t {
         const int64_t row = sw * RPS + r;
         return (uact && row < row_stop) ? (uint32_t)((row - row_begin) * rowbytes + unit_off)
                                         : kOutOfRange;
     };
 
+    // ---- activation loads go out first, then the first D sweeps ----
+    // XS_LDS: this thread's first group of 8 activations (the first pass of
+    // the cooperative conversion); XS_THREAD / XS_F32: the unit's 64 floats.
+    const int ngroups = (int)(cols / 8);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(cols * 4));
+    uint4 xv[XS == XS_LDS ? 2 : 16];
+    if (XS == XS_LDS) {
+        const uint32_t xo = t < ngroups ? (uint32_t)t * 32u : kOutOfRange;
+        xv[0] = bload16(rx, xo);
+        xv[1] = bload16(rx, xo + 16u);
+    } else {
+        const uint32_t xo = uact ? (uint32_t)(64 * u) * 4u : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xo + 16u * i);
+    }
+
     Slot<NMAT> buf[D + 1];
 #pragma unroll
     for (int j = 0; j < D; ++j) load_slot<NMAT>(buf[j], rs, slot_off(s_begin + j), qoff);
 
-    // The thread's 64 activations: x[256b + 64g + 0..31] (sub-block A) and
-    // x[256b + 64g + 32..63] (sub-block B), loaded once.
-    // Unused units read zeros (out-of-range offset).
-    float xa[32], xb[32];
-    float SA = 0.f, SB = 0.f;
-    {
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.nb * 1024u);
-        const uint32_t xo = uact ? (uint32_t)(256 * b + 64 * g) * 4u : kOutOfRange;
+    // ---- the thread's activations (unused units: zeros) ----
+    XUnit xu;
+    XF32 xf;
+    if (XS == XS_THREAD || XS == XS_F32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint4 va = bload16(rx, xo + 16u * i);
-            const uint4 vb = bload16(rx, xo + 128u + 16u * i);
-            xa[4 * i + 0] = __uint_as_float(va.x); xa[4 * i + 1] = __uint_as_float(va.y);
-            xa[4 * i + 2] = __uint_as_float(va.z); xa[4 * i + 3] = __uint_as_float(va.w);
-            xb[4 * i + 0] = __uint_as_float(vb.x); xb[4 * i + 1] = __uint_as_float(vb.y);
-            xb[4 * i + 2] = __uint_as_float(vb.z); xb[4 * i + 3] = __uint_as_float(vb.w);
+            xf.xa[4 * i + 0] = __uint_as_float(xv[i].x); xf.xa[4 * i + 1] = __uint_as_float(xv[i].y);
+            xf.xa[4 * i + 2] = __uint_as_float(xv[i].z); xf.xa[4 * i + 3] = __uint_as_float(xv[i].w);
+            xf.xb[4 * i + 0] = __uint_as_float(xv[8 + i].x); xf.xb[4 * i + 1] = __uint_as_float(xv[8 + i].y);
+            xf.xb[4 * i + 2] = __uint_as_float(xv[8 + i].z); xf.xb[4 * i + 3] = __uint_as_float(xv[8 + i].w);
         }
+        if (XS == XS_THREAD) {
+            planes32(xf.xa, xu.pa, xu.XA, xu.SA);
+            planes32(xf.xb, xu.pb, xu.XB, xu.SB);
+        } else {
+            xf.SA = xf.SB = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            SA += xa[i];
-            SB += xb[i];
+            for (int i = 0; i < 32; ++i) {
+                xf.SA += xf.xa[i];
+                xf.SB += xf.xb[i];
+            }
+        }
+    } else {
+        // Cooperative conversion: 4 threads per 32-activation sub-block, 8
+        // activations each; max and sum over the 4 lanes by xor shuffles.
+        float *Xs = reinterpret_cast<float *>(xlds + 3 * cols);
+        float *Ss = Xs + cols / 32;
+        for (int e0 = 0; e0 < ngroups; e0 += blockDim.x) {
+            const int e = e0 + t;   // uniform trip count; blockDim % 4 == 0
+            if (e0 > 0) {
+                const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
+                xv[0] = bload16(rx, xo);
+                xv[1] = bload16(rx, xo + 16u);
+            }
+            const float v[8] = {__uint_as_float(xv[0].x), __uint_as_float(xv[0].y),
+                                __uint_as_float(xv[0].z), __uint_as_float(xv[0].w),
+                                __uint_as_float(xv[1].x), __uint_as_float(xv[1].y),
+                                __uint_as_float(xv[1].z), __uint_as_float(xv[1].w)};
+            float amax = 0.f, sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                amax = fmaxf(amax, fabsf(v[i]));
+                sum += v[i];
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            sum += __shfl_xor(sum, 1);
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            sum += __shfl_xor(sum, 2);
+            int shift;
+            float X;
+            bfp_params(amax, sum, shift, X);
+            uint32_t p[3][2];
+            pack4((uint32_t)to_int22(v[0], shift), (uint32_t)to_int22(v[1], shift),
+                  (uint32_t)to_int22(v[2], shift), (uint32_t)to_int22(v[3], shift), p[0][0],
+                  p[1][0], p[2][0]);
+            pack4((uint32_t)to_int22(v[4], shift), (uint32_t)to_int22(v[5], shift),
+                  (uint32_t)to_int22(v[6], shift), (uint32_t)to_int22(v[7], shift), p[0][1],
+                  p[1][1], p[2][1]);
+            if (e < ngroups) {
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+                    *reinterpret_cast<uint2 *>(xlds + pl * cols + 8 * e) =
+                        make_uint2(p[pl][0], p[pl][1]);
+                if ((e & 3) == 0) {
+                    Xs[e >> 2] = X;
+                    Ss[e >> 2] = sum;
+                }
+            }
+        }
+        __syncthreads();
+        // This unit's planes: 64 bytes per plane at 64u, X and S at 2u.
+        if (uact) {
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) {
+                const uint4 *q = reinterpret_cast<const uint4 *>(xlds + pl * cols + 64 * u);
+                const uint4 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
+                xu.pa[pl][0] = v0.x; xu.pa[pl][1] = v0.y; xu.pa[pl][2] = v0.z; xu.pa[pl][3] = v0.w;
+                xu.pa[pl][4] = v1.x; xu.pa[pl][5] = v1.y; xu.pa[pl][6] = v1.z; xu.pa[pl][7] = v1.w;
+                xu.pb[pl][0] = v2.x; xu.pb[pl][1] = v2.y; xu.pb[pl][2] = v2.z; xu.pb[pl][3] = v2.w;
+                xu.pb[pl][4] = v3.x; xu.pb[pl][5] = v3.y; xu.pb[pl][6] = v3.z; xu.pb[pl][7] = v3.w;
+            }
+            xu.XA = Xs[2 * u];
+            xu.XB = Xs[2 * u + 1];
+            xu.SA = Ss[2 * u];
+            xu.SB = Ss[2 * u + 1];
+        } else {
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xu.pa[pl][i] = xu.pb[pl][i] = 0u;
+            xu.XA = xu.XB = xu.SA = xu.SB = 0.f;
         }
     }
 
+    // One sweep: dot products, wave reduction, and every fb sweeps the
+    // cross-wave reduction and epilogue of that batch of rows.
     int kb = 0, bank = 0;
-    for (int64_t s = s_begin; s < s_end; s += D + 1) {
+    auto compute_sweep = [&](const Slot<NMAT> &sl, int64_t sj) {
 #pragma unroll
-        for (int j = 0; j <= D; ++j) {
-            const int64_t sj = s + j;
-            if (sj >= s_end) break;  // uniform
-            // the next sweep's loads go out before this sweep is computed;
-            // past the end they read zeros (unused)
-            if (D > 0) load_slot<NMAT>(buf[(j + D) % (D + 1)], rs, slot_off(sj + D), qoff);
-            if (D == 0) load_slot<NMAT>(buf[0], rs, slot_off(sj), qoff);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                float v = unit_dot(buf[j].q[m], buf[j].h[m], xa, xb, SA, SB, sh, upper);
-#pragma unroll
-                for (int off = RPS; off < 64; off <<= 1) v += __shfl_xor(v, off);
-                if (lane < RPS) red[bank][wave][(kb * NMAT + m) * RPS + lane] = v;
-            }
-            ++kb;
-            if (kb == FB || sj == s_end - 1) {
-                __syncthreads();
-                if (t < kb * RPS) {
-                    const int k = t / RPS, rr = t % RPS;
-                    const int64_t row = (sj - kb + 1 + k) * RPS + rr;
-                    if (row < row_stop) {
-                        float v0 = 0.f, v1 = 0.f;
-                        for (int w = 0; w < nwaves; ++w) {
-                            v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
-                            if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
-                        }
-                        if (EPI == EPI_STORE) {
-                            if (row < a.split0)
-                                a.o0[row] = v0;
-                            else if (row < a.split1)
-                                a.o1[row - a.split0] = v0;
-                            else
-                                a.o2[row - a.split1] = v0;
-                        } else if (EPI == EPI_GATE_UP) {
-                            a.o0[row] = act_apply(v0, a.act) * v1;
-                        } else {
+        for (int m = 0; m < NMAT; ++m) {
+            float v = kInt ? unit_dot(sl.q[m], sl.h[m], xu, sh, upper)
+                           : unit_dot_f32(sl.q[m], sl.h[m], xf, sh, upper);
+            v = wave_sum_mod<RPS>(v);
+            if (lane < RPS) red[bank][wave][(kb * NMAT + m) * RPS + lane] = v;
+        }
+        ++kb;
+        if (kb == fb || sj == s_end - 1) {
+            __syncthreads();
+            if (t < kb * RPS) {
+                const int k = t / RPS, rr = t % RPS;
+                const int64_t row = (sj - kb + 1) * RPS + t;
+                if (row < row_stop) {
+                    float v0 = 0.f, v1 = 0.f;
+                    for (int w = 0; w < nwaves; ++w) {
+                        v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
+                        if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
+                    }
+                    if (EPI == EPI_STORE) {
+                        if (row < a.split0)
                             a.o0[row] = v0;
-                            lg[row - row_begin] = v0;
-                            taken[row - row_begin] = 0;
-                        }
+                        else if (row < a.split1)
+                            a.o1[row - a.split0] = v0;
+                        else
+                            a.o2[row - a.split1] = v0;
+                    } else if (EPI == EPI_GATE_UP) {
+                        a.o0[row] = act_apply(v0, a.act) * v1;
+                    } else {
+                        a.o0[row] = v0;
+                        lg[row - row_begin] = v0;
+                        taken[row - row_begin] = 0;
                     }
                 }
-                kb = 0;
-                bank ^= 1;
             }
+            kb = 0;
+            bank ^= 1;
+        }
+    };
+
+    // Full groups of D+1 sweeps: step j issues sweep s+j+D into the slot freed
+    // by step j-1 and computes sweep s+j. No early exit inside a group keeps
+    // the ring's wait counts exact (only the oldest sweep is waited for).
+    // Prefetches past the workgroup's last sweep read zeros.
+    int64_t s = s_begin;
+    for (; s + D < s_end; s += D + 1) {
+#pragma unroll
+        for (int j = 0; j <= D; ++j) {
+            if (D > 0) load_slot<NMAT>(buf[(j + D) % (D + 1)], rs, slot_off(s + j + D), qoff);
+            if (D == 0) load_slot<NMAT>(buf[0], rs, slot_off(s + j), qoff);
+            compute_sweep(buf[j], s + j);
+        }
+    }
+    // Tail: fewer than D+1 sweeps left, all already in flight in buf[0..].
+#pragma unroll
+    for (int j = 0; j < (D > 0 ? D : 1); ++j) {
+        if (s + j < s_end) {
+            if (D == 0) load_slot<NMAT>(buf[0], rs, slot_off(s + j), qoff);
+            compute_sweep(buf[j], s + j);
         }
     }
 
@@ -425,6 +722,9 @@ Shape pick_shape(int64_t cols)
     return {rps, threads};
 }
 
+// Activations go through LDS up to this many columns (planes_bytes <= 52 KB).
+constexpr int64_t kLdsColsMax = 16384;
+
 // Compute units of the current device (cached per device).
 int device_cus()
 {
@@ -441,28 +741,23 @@ int device_cus()
     return cache[dev];
 }
 
-// Workgroups of `threads` threads resident per CU for a kernel using ~vgprs
-// registers per lane (512 per SIMD lane, 4 SIMDs, wave64).
-int wgs_per_cu(int threads, int vgprs)
-{
-    const int waves_per_simd = 512 / vgprs;
-    const int waves = (threads + 63) / 64;
-    const int per_cu = (4 * waves_per_simd) / waves;
-    return per_cu < 1 ? 1 : per_cu;
-}
-
-template <int NMAT, int EPI, int D>
+template <int NMAT, int EPI, int XS, int D>
 hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s)
 {
     const dim3 grid((unsigned)nwg), block((unsigned)threads);
+    const int64_t cols = (int64_t)a.nb * kQK;
+    const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols) : 0;
     if (threads > 512) {
-        // only reachable with one row per sweep (cols > 32768)
-        hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, 1024, 0>), grid, block, 0, s, a);
+        // only reachable with one row per sweep (cols > 32768: no LDS planes)
+        hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, XS == XS_LDS ? XS_THREAD : XS, 1024, 0>),
+                           grid, block, 0, s, a);
         return hipGetLastError();
     }
     switch (rps) {
-#define Q4K_RPS_CASE(R) \
-    case R: hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, 512, D>), grid, block, 0, s, a); break;
+#define Q4K_RPS_CASE(R)                                                                       \
+    case R:                                                                                   \
+        hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, XS, 512, D>), grid, block, lds, s, a); \
+        break;
         Q4K_RPS_CASE(1)
         Q4K_RPS_CASE(2)
         Q4K_RPS_CASE(4)
@@ -476,6 +771,16 @@ hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hip
     return hipGetLastError();
 }
 
+// Block-floating-point activations: converted in LDS when they fit, else per
+// thread.
+template <int NMAT, int EPI, int D>
+hipError_t launch_rows_bfp(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s)
+{
+    if ((int64_t)a.nb * kQK <= kLdsColsMax)
+        return launch_rows<NMAT, EPI, XS_LDS, D>(a, rps, threads, nwg, s);
+    return launch_rows<NMAT, EPI, XS_THREAD, D>(a, rps, threads, nwg, s);
+}
+
 RowsArgs base_args(int64_t rows, int64_t cols)
 {
     RowsArgs a{};
@@ -487,22 +792,22 @@ RowsArgs base_args(int64_t rows, int64_t cols)
     return a;
 }
 
-// Persistent grid: as many workgroups as fit on the device at once, never
-// more than there are sweeps, and enough that one workgroup's rows span less
-// than 2^30 bytes (its buffer resource uses 32-bit offsets).
-int64_t grid_for(int64_t rows, int64_t cols, const Shape &sh, int vgprs)
+// Grid: about `per_cu` workgroups per compute unit, never more than there are
+// sweeps, and enough that one workgroup's rows span less than 2^30 bytes (its
+// buffer resource uses 32-bit offsets).
+int64_t grid_for(int64_t rows, int64_t cols, const Shape &sh, int per_cu)
 {
     const int64_t S = (rows + sh.rps - 1) / sh.rps;
-    int64_t g = (int64_t)device_cus() * wgs_per_cu(sh.threads, vgprs);
+    int64_t g = (int64_t)device_cus() * per_cu;
     const int64_t sweep_bytes = (int64_t)sh.rps * (cols / kQK) * kBlockBytes;
-    const int64_t max_sweeps = ((int64_t)1 << 30) / sweep_bytes;   // >= 1 for cols <= 65536
-    const int64_t min_g = (S + max_sweeps - 2) / (max_sweeps - 1 > 0 ? max_sweeps - 1 : 1);
+    int64_t max_sweeps = ((int64_t)1 << 30) / sweep_bytes;
+    if (max_sweeps < 2) max_sweeps = 2;
+    const int64_t min_g = (S + max_sweeps - 2) / (max_sweeps - 1);
     if (g < min_g) g = min_g;
     return S < g ? S : g;
 }
 
-constexpr int kVgprStore = 168;   // budget the kernels are written to (3 waves/SIMD)
-constexpr int kLmheadWgs = 512;   // device-independent: fixes the workspace size
+constexpr int kLmheadWgsMax = 1024;  // bounds the candidate workspace
 
 }  // namespace
 
@@ -519,7 +824,8 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     a.split0 = split0;
     a.split1 = split1;
     const Shape sh = pick_shape(cols);
-    return launch_rows<1, EPI_STORE, 3>(a, sh.rps, sh.threads, grid_for(rows, cols, sh, kVgprStore), s);
+    return launch_rows_bfp<1, EPI_STORE, Q4K_STORE_D>(a, sh.rps, sh.threads,
+                                                      grid_for(rows, cols, sh, Q4K_STORE_WGS_PER_CU), s);
 }
 
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
@@ -532,8 +838,23 @@ hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, 
     a.o0 = h;
     a.act = act;
     const Shape sh = pick_shape(cols);
-    return launch_rows<2, EPI_GATE_UP, 1>(a, sh.rps, sh.threads, grid_for(rows, cols, sh, kVgprStore),
-                                          s);
+    return launch_rows_bfp<2, EPI_GATE_UP, Q4K_GATE_UP_D>(
+        a, sh.rps, sh.threads, grid_for(rows, cols, sh, Q4K_GATE_UP_WGS_PER_CU), s);
+}
+
+hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
+                      float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s)
+{
+    hipError_t e = launch_gate_up(Wg, Wu, x, h, inter, hidden, act, s);
+    if (e != hipSuccess) return e;
+    // down projection: few rows per thread, so f32 activations (no conversion)
+    RowsArgs b = base_args(hidden, inter);
+    b.W0 = Wd;
+    b.x = h;
+    b.o0 = y;
+    const Shape sd = pick_shape(inter);
+    return launch_rows<1, EPI_STORE, XS_F32, Q4K_DOWN_D>(
+        b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s);
 }
 
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols)
@@ -541,7 +862,18 @@ int64_t lmhead_num_wgs(int64_t rows, int64_t cols)
     const Shape sh = pick_shape(cols);
     const int64_t S = (rows + sh.rps - 1) / sh.rps;
     // enough workgroups that each holds at most kLmheadRowsPerWgMax rows
-    int64_t g = kLmheadWgs;
+    int64_t g = (int64_t)device_cus() * Q4K_LMHEAD_WGS_PER_CU;
+    if (g > kLmheadWgsMax) g = kLmheadWgsMax;
+    const int64_t min_g = (S * sh.rps + kLmheadRowsPerWgMax - 1) / (kLmheadRowsPerWgMax - sh.rps);
+    if (g < min_g) g = min_g;
+    return S < g ? S : g;
+}
+
+int64_t lmhead_max_wgs(int64_t rows, int64_t cols)
+{
+    const Shape sh = pick_shape(cols);
+    const int64_t S = (rows + sh.rps - 1) / sh.rps;
+    int64_t g = kLmheadWgsMax;
     const int64_t min_g = (S * sh.rps + kLmheadRowsPerWgMax - 1) / (kLmheadRowsPerWgMax - sh.rps);
     if (g < min_g) g = min_g;
     return S < g ? S : g;
@@ -559,7 +891,7 @@ hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, i
     a.k = k;
     const Shape sh = pick_shape(cols);
     const int64_t nwg = lmhead_num_wgs(rows, cols);
-    hipError_t e = launch_rows<1, EPI_LOGITS, 3>(a, sh.rps, sh.threads, nwg, s);
+    hipError_t e = launch_rows_bfp<1, EPI_LOGITS, Q4K_LMHEAD_D>(a, sh.rps, sh.threads, nwg, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeThreads), 0, s, cand, (int)nwg, k,
                        logits, top_idx, top_val);

@@ -77,7 +77,8 @@ def test_single_hot_probes_recover_every_weight(q4k, orc):
 
 @pytest.mark.parametrize("rows,cols", [(1, 256), (7, 256), (33, 768), (100, 1280), (1000, 2560),
                                        (257, 4096), (65, 10240), (3, 40960), (5, 65536),
-                                       (513, 2304), (40, 512)])
+                                       (513, 2304), (40, 512), (100000, 256), (70001, 512),
+                                       (4099, 16384), (129, 20480), (64, 32768)])
 def test_matvec_ragged_shapes(q4k, orc, rows, cols):
     rng = np.random.default_rng(rows * 7919 + cols)
     W = inputs.q4k_random(rng, rows, cols)
@@ -208,7 +209,8 @@ def test_ffn_all_34_layers(q4k, orc):
 
 
 @pytest.mark.parametrize("act", [0, 1])
-@pytest.mark.parametrize("hidden,inter", [(256, 256), (512, 1280), (768, 2304)])
+@pytest.mark.parametrize("hidden,inter", [(256, 256), (512, 1280), (768, 2304), (256, 65536),
+                                          (20480, 512), (2560, 33024)])
 def test_ffn_small_shapes_both_activations(q4k, orc, act, hidden, inter):
     rng = np.random.default_rng(hidden + inter + act)
     Wg = inputs.q4k_random(rng, inter, hidden)
@@ -267,7 +269,8 @@ def test_lmhead_config_top5(q4k, orc):
 
 
 @pytest.mark.parametrize("rows,cols,k", [(1, 256, 1), (64, 512, 64), (100, 256, 7),
-                                         (4097, 512, 64), (30000, 1024, 5), (20000, 768, 33)])
+                                         (4097, 512, 64), (30000, 1024, 5), (20000, 768, 33),
+                                         (100000, 256, 5), (3000, 20480, 9)])
 def test_lmhead_shapes_and_k(q4k, orc, rows, cols, k):
     rng = np.random.default_rng(rows + cols + k)
     W = inputs.q4k_random(rng, rows, cols)
