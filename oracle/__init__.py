@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.q4o_matmul.argtypes = [P, P, I64, I64, I64, P, P]
         L.q4o_ffn_prefill.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P, P]
         L.q4o_ffn_prefill_bf16.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P, P]
+        L.q4o_matmul_bf16.argtypes = [P, P, I64, I64, I64, P, P]
+        L.q4o_act_deriv.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.q4o_act_deriv.restype = ctypes.c_double
+        L.q4o_ffn_prefill_scale.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         L.q4o_round_bf16.argtypes = [ctypes.c_double]
         L.q4o_round_bf16.restype = ctypes.c_double
         _lib = L
@@ -197,6 +201,20 @@ def matmul(W, X, rows: int, cols: int):
     return Y, A
 
 
+def matmul_bf16(W, X, rows: int, cols: int):
+    """(Y, A) of W X[t] with bf16 operands (X rounded; W formed in binary32, then
+    rounded) and exact f64 products and sums: the matrix-core operand model."""
+    W = _u8(W)
+    _check_w(W, rows, cols)
+    X = _f32(X)
+    seq = X.size // cols
+    assert X.size == seq * cols
+    Y = np.zeros((seq, rows), np.float64)
+    A = np.zeros((seq, rows), np.float64)
+    lib().q4o_matmul_bf16(_ptr(W), _ptr(X), seq, rows, cols, _ptr(Y), _ptr(A))
+    return Y, A
+
+
 def ffn_prefill(Wg, Wu, Wd, X, hidden: int, inter: int, act: int = GELU_TANH):
     Wg, Wu, Wd = _u8(Wg), _u8(Wu), _u8(Wd)
     X = _f32(X)
@@ -206,6 +224,23 @@ def ffn_prefill(Wg, Wu, Wd, X, hidden: int, inter: int, act: int = GELU_TANH):
     lib().q4o_ffn_prefill(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(X), seq, hidden, inter, int(act),
                           _ptr(Y), _ptr(A))
     return Y, A
+
+
+def act_deriv(z: float, act: int) -> float:
+    return lib().q4o_act_deriv(float(z), int(act))
+
+
+def ffn_prefill_scale(Wg, Wu, Wd, X, hidden: int, inter: int, act: int = GELU_TANH):
+    """Per-output error scale Ap [seq, hidden] of the gated FFN under relative
+    operand rounding: sum_j |wd_ij| (|act'(g_j) u_j| A_g,j + |act(g_j)| A_u,j
+    + 2 |h_j|). Never below the last stage's plain A."""
+    Wg, Wu, Wd = _u8(Wg), _u8(Wu), _u8(Wd)
+    X = _f32(X)
+    seq = X.size // hidden
+    Ap = np.zeros((seq, hidden), np.float64)
+    lib().q4o_ffn_prefill_scale(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(X), seq, hidden, inter,
+                                int(act), _ptr(Ap))
+    return Ap
 
 
 def ffn_prefill_bf16(Wg, Wu, Wd, X, hidden: int, inter: int, act: int = GELU_TANH):

@@ -181,6 +181,62 @@ void q4o_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const floa
     free(h);
 }
 
+/* Derivatives of the activations, written from their definitions:
+ * gelu_tanh(z) = 0.5 z (1 + t), t = tanh(c (z + 0.044715 z^3)), c = sqrt(2/pi):
+ *   d/dz = 0.5 (1 + t) + 0.5 z (1 - t^2) c (1 + 3 * 0.044715 z^2);
+ * silu(z) = z s, s = 1 / (1 + e^-z):  d/dz = s (1 + z (1 - s)). */
+double q4o_act_deriv(double z, int act)
+{
+    if (act == 0) {
+        const double c = sqrt(2.0 / M_PI);
+        const double t = tanh(c * (z + 0.044715 * z * z * z));
+        return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * z * z);
+    }
+    const double s = 1.0 / (1.0 + exp(-z));
+    return s * (1.0 + z * (1.0 - s));
+}
+
+/* Error scale of the gated FFN under relative rounding of its operands. With
+ * A_g = sum_k |wg_jk x_k| and A_u likewise, a relative change of at most e in
+ * every x, wg, wu and wd, and in h, moves y_i by at most, to first order,
+ *   e * sum_j |wd_ij| (|act'(g_j) u_j| A_g,j + |act(g_j)| A_u,j + 2 |h_j|)
+ * (the last term counts wd's and h's own rounding). Ap returns that factor of
+ * e per token and output, [seq][hidden]; it is the tolerance scale of the
+ * reduced-precision FFN, and it is never below the plain A of the last stage. */
+void q4o_ffn_prefill_scale(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd,
+                           const float *X, int64_t seq, int64_t hidden, int64_t inter, int act,
+                           double *Ap)
+{
+    double *g = (double *)malloc((size_t)inter * sizeof(double));
+    double *u = (double *)malloc((size_t)inter * sizeof(double));
+    double *ag = (double *)malloc((size_t)inter * sizeof(double));
+    double *au = (double *)malloc((size_t)inter * sizeof(double));
+    double *m = (double *)malloc((size_t)inter * sizeof(double));
+    double *wd = (double *)malloc((size_t)inter * sizeof(double));
+    for (int64_t t = 0; t < seq; ++t) {
+        const float *x = X + t * hidden;
+        q4o_matvec(Wg, x, inter, hidden, g, ag);
+        q4o_matvec(Wu, x, inter, hidden, u, au);
+        for (int64_t j = 0; j < inter; ++j) {
+            const double a = act == 0 ? q4o_gelu_tanh(g[j]) : q4o_silu(g[j]);
+            m[j] = fabs(q4o_act_deriv(g[j], act) * u[j]) * ag[j] + fabs(a) * au[j] +
+                   2.0 * fabs(a * u[j]);
+        }
+        for (int64_t i = 0; i < hidden; ++i) {
+            q4o_dequant(Wd + i * (inter / 256) * 144, 1, inter, wd);
+            double acc = 0.0;
+            for (int64_t j = 0; j < inter; ++j) acc += fabs(wd[j]) * m[j];
+            Ap[t * hidden + i] = acc;
+        }
+    }
+    free(g);
+    free(u);
+    free(ag);
+    free(au);
+    free(m);
+    free(wd);
+}
+
 /* ---- top-k: the first k entries of all rows ordered by (value descending,
  * index ascending); NaN values rank below every number, among themselves by
  * index. A full sort is the definition. ---- */
@@ -249,6 +305,33 @@ double q4o_round_bf16(double v)
     float r;
     memcpy(&r, &bits, sizeof r);
     return (double)r;
+}
+
+/* Matrix product with bf16 operands: X rounded to bf16, W formed in binary32
+ * and rounded to bf16, products and sums exact (f64). A as in q4o_matmul but
+ * from the bf16 operands. A tighter second check of the matrix-core path. */
+void q4o_matmul_bf16(const uint8_t *W, const float *X, int64_t seq, int64_t rows, int64_t cols,
+                     double *Y, double *A)
+{
+    double *w = (double *)malloc((size_t)cols * sizeof(double));
+    double *xb = (double *)malloc((size_t)(seq * cols) * sizeof(double));
+    for (int64_t i = 0; i < seq * cols; ++i) xb[i] = q4o_round_bf16((double)X[i]);
+    for (int64_t i = 0; i < rows; ++i) {
+        q4o_dequant(W + i * (cols / 256) * 144, 1, cols, w);
+        for (int64_t j = 0; j < cols; ++j) w[j] = q4o_round_bf16(q4o_round_f32(w[j]));
+        for (int64_t t = 0; t < seq; ++t) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < cols; ++j) {
+                const double p = w[j] * xb[t * cols + j];
+                acc += p;
+                mag += fabs(p);
+            }
+            Y[t * rows + i] = acc;
+            if (A) A[t * rows + i] = mag;
+        }
+    }
+    free(w);
+    free(xb);
 }
 
 /* Per-token gated FFN with bf16 operands: X and W rounded to bf16 (W via

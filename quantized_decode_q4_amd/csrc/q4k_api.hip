@@ -38,6 +38,7 @@ int64_t wbytes(int64_t rows, int64_t cols) { return rows * (cols / Q4K_QK) * Q4K
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int64_t kMfmaMinSeq = 64;  // seq at which prefill switches to the matrix cores
+constexpr int64_t kSeqMax = 64 * 65535;  // 64-token groups on one grid dimension
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -181,14 +182,16 @@ Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int
 Q4K_EXPORT size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq)
 {
     if (!rows_ok(rows) || !cols_ok(cols) || seq < 0) return 0;
-    if (seq < kMfmaMinSeq) return 0;
-    return round_up((size_t)seq * (size_t)cols * 2, 256);
+    if (seq < kMfmaMinSeq || rows == 0) return 0;
+    const q4k::MmPlan pl = q4k::mm_plan(rows, cols, seq, 1);
+    return round_up((size_t)q4k::mm_frag_bytes(seq, cols), 256) +
+           round_up((size_t)q4k::mm_partial_bytes(pl, seq, rows, 1), 256);
 }
 
 Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
                           int64_t seq, void *ws, size_t ws_bytes, void *stream)
 {
-    if (!rows_ok(rows) || !cols_ok(cols) || seq < 0 || seq > INT32_MAX) return Q4K_ERR_SHAPE;
+    if (!rows_ok(rows) || !cols_ok(cols) || seq < 0 || seq > kSeqMax) return Q4K_ERR_SHAPE;
     if (rows == 0 || seq == 0) return Q4K_OK;
     if (!W || !X || !Y) return Q4K_ERR_NULL;
     if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return Q4K_ERR_ALIGN;
@@ -201,6 +204,12 @@ Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows,
     for (int j = 0; j < 2; ++j)
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
+    if (seq >= kMfmaMinSeq) {
+        uint8_t *w8 = (uint8_t *)ws;
+        float *partial = (float *)(w8 + round_up((size_t)q4k::mm_frag_bytes(seq, cols), 256));
+        return hip_status(q4k::launch_matmul_mfma((const uint8_t *)W, X, Y, rows, cols, seq, w8,
+                                                  partial, s));
+    }
     // f32 path: one matvec per token (every token re-reads W).
     for (int64_t t = 0; t < seq; ++t) {
         const int st = hip_status(q4k::launch_rows_store((const uint8_t *)W, X + t * cols,
@@ -216,8 +225,13 @@ Q4K_EXPORT size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, i
     if (seq < 0 || !cols_ok(hidden) || !cols_ok(inter)) return 0;
     size_t need = round_up((size_t)inter * 4, 256);
     if (seq >= kMfmaMinSeq) {
-        const size_t mm = round_up((size_t)seq * (size_t)hidden * 2, 256) +
-                          round_up((size_t)seq * (size_t)inter * 2, 256);
+        const q4k::MmPlan pg = q4k::mm_plan(inter, hidden, seq, 2);
+        const q4k::MmPlan pd = q4k::mm_plan(hidden, inter, seq, 1);
+        const int64_t pa = q4k::mm_partial_bytes(pg, seq, inter, 2);
+        const int64_t pb = q4k::mm_partial_bytes(pd, seq, hidden, 1);
+        const size_t mm = round_up((size_t)q4k::mm_frag_bytes(seq, hidden), 256) +
+                          round_up((size_t)q4k::mm_frag_bytes(seq, inter), 256) +
+                          round_up((size_t)(pa > pb ? pa : pb), 256);
         need = mm > need ? mm : need;
     }
     return need;
@@ -227,7 +241,7 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
                                float *Y, int64_t seq, int64_t hidden, int64_t inter, int act,
                                void *ws, size_t ws_bytes, void *stream)
 {
-    if (seq < 0 || seq > INT32_MAX || !cols_ok(hidden) || !cols_ok(inter)) return Q4K_ERR_SHAPE;
+    if (seq < 0 || seq > kSeqMax || !cols_ok(hidden) || !cols_ok(inter)) return Q4K_ERR_SHAPE;
     if (act != Q4K_ACT_GELU_TANH && act != Q4K_ACT_SILU) return Q4K_ERR_ACT;
     if (seq == 0) return Q4K_OK;
     if (!Wg || !Wu || !Wd || !X || !Y) return Q4K_ERR_NULL;
@@ -244,6 +258,14 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
     for (int j = 0; j < 4; ++j)
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
+    if (seq >= kMfmaMinSeq) {
+        uint8_t *xf = (uint8_t *)ws;
+        uint8_t *hf = xf + round_up((size_t)q4k::mm_frag_bytes(seq, hidden), 256);
+        float *partial = (float *)(hf + round_up((size_t)q4k::mm_frag_bytes(seq, inter), 256));
+        return hip_status(q4k::launch_ffn_prefill_mfma((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                                       (const uint8_t *)Wd, X, Y, seq, hidden,
+                                                       inter, act, xf, hf, partial, s));
+    }
     for (int64_t t = 0; t < seq; ++t) {
         const int st = hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                                   (const uint8_t *)Wd, X + t * hidden,

@@ -426,6 +426,72 @@ def test_bf16_prefill_model_close_to_exact(orc):
     assert err.max() > 1e-7    # the rounding is really applied
 
 
+def test_bf16_matmul_model_exact_on_bf16_operands(orc):
+    """With every weight and activation already bf16-exact (d a power of two,
+    dmin 0, scale*quant below 256; activations k/8), the bf16 operand model and
+    the exact product coincide bit for bit."""
+    rng = np.random.default_rng(19)
+    rows, cols, seq = 12, 512, 3
+    blocks = []
+    for _ in range(rows * cols // 256):
+        sc = rng.integers(0, 16, 8)
+        q = rng.integers(0, 16, 256)
+        blocks.append(pack_block(2.0 ** -10, 0.0, sc, np.zeros(8, int), q))
+    W = np.concatenate(blocks).reshape(rows, -1)
+    X = (rng.integers(-64, 65, (seq, cols)) / 8.0).astype(np.float32)
+    Y, A = orc.matmul(W, X, rows, cols)
+    Yb, Ab = orc.matmul_bf16(W, X, rows, cols)
+    assert np.array_equal(Y, Yb) and np.array_equal(A, Ab)
+
+
+def test_bf16_matmul_model_within_rounding_bound(orc):
+    """Each bf16 operand carries relative error <= 2^-9 (the weight after its
+    binary32 rounding), so every product is off by at most 2^-8 + 2^-17 of its
+    magnitude and |Y_bf16 - Y| <= (2^-8 + 2^-17) A."""
+    rng = np.random.default_rng(20)
+    rows, cols, seq = 50, 1024, 4
+    W = inputs.q4k_random(rng, rows, cols)
+    X = rng.standard_normal((seq, cols)).astype(np.float32)
+    Y, A = orc.matmul(W, X, rows, cols)
+    Yb, _ = orc.matmul_bf16(W, X, rows, cols)
+    err = np.abs(Yb - Y) / A
+    assert err.max() <= 2.0 ** -8 + 2.0 ** -17
+    assert err.max() > 1e-6
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_activation_derivative_matches_finite_differences(orc, act):
+    f = orc.gelu_tanh if act == 0 else orc.silu
+    hstep = 1e-5
+    for z in np.linspace(-8.0, 8.0, 161):
+        fd = (f(z + hstep) - f(z - hstep)) / (2 * hstep)
+        assert abs(orc.act_deriv(z, act) - fd) < 1e-8, (z, act)
+    assert orc.act_deriv(0.0, act) == 0.5          # both: f'(0) = 1/2
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_ffn_error_scale_bounds_input_perturbations(orc, act):
+    """Relative perturbations of X of at most e move y by at most e * Ap (to
+    first order), and Ap is never below the last stage's plain A."""
+    rng = np.random.default_rng(21 + act)
+    hidden, inter, seq = 256, 512, 3
+    Wg = inputs.q4k_random(rng, inter, hidden)
+    Wu = inputs.q4k_random(rng, inter, hidden)
+    Wd = inputs.q4k_random(rng, hidden, inter)
+    X = rng.standard_normal((seq, hidden)).astype(np.float32)
+    Y, A = orc.ffn_prefill(Wg, Wu, Wd, X, hidden, inter, act)
+    Ap = orc.ffn_prefill_scale(Wg, Wu, Wd, X, hidden, inter, act)
+    assert np.all(Ap >= A)
+    e = 1e-4
+    worst = 0.0
+    for _ in range(6):
+        Xp = (X.astype(np.float64) * (1 + rng.uniform(-e, e, X.shape))).astype(np.float32)
+        Yp, _ = orc.ffn_prefill(Wg, Wu, Wd, Xp, hidden, inter, act)
+        worst = max(worst, float((np.abs(Yp - Y) / (e * Ap)).max()))
+    assert worst <= 1.0, worst
+    assert worst > 1e-3                                # the scale is not vacuous
+
+
 def test_generator_is_deterministic_and_layout_sized():
     a = inputs.tiny_matvec()
     b = inputs.tiny_matvec()
