@@ -8,6 +8,9 @@ before timing; 34 distinct layers exceed the 256 MB Infinity Cache, so each
 step streams its weights from HBM. Steps are replayed from HIP graphs captured
 once (launch-bound inner loop); the eager launch rate is reported beside it.
 
+Beside the step, the 64-token prefill FFN on the same 34 layers' weights (the
+matrix-core path) is timed per call and reported with its MFMA utilisation.
+
 Prints ONE JSON line (see the fields at the end of main()).
 """
 from __future__ import annotations
@@ -45,15 +48,21 @@ DOWN_BYTES = wbytes(HIDDEN, INTER) + INTER * 4 + HIDDEN * 4
 LAYER_BYTES = QKV_BYTES + GATE_UP_BYTES + DOWN_BYTES
 LMHEAD_BYTES = wbytes(VOCAB, HIDDEN) + HIDDEN * 4 + VOCAB * 4 + TOPK * 8
 STEP_BYTES = LAYERS * LAYER_BYTES + LMHEAD_BYTES
+# Prefill FFN, 64 tokens: weights once, X in, Y out; 2 flops per weight per token.
+PREFILL_SEQ = 64
+PREFILL_BYTES = 3 * wbytes(INTER, HIDDEN) + 2 * PREFILL_SEQ * HIDDEN * 4
+PREFILL_FLOPS = 2 * PREFILL_SEQ * 3 * INTER * HIDDEN
 
 
 def source_digest() -> str:
+    """Digest of the translation unit that holds the decode kernels (the
+    dominant kernel's source): counter figures taken from other code are not
+    reported as this code's traffic."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "quantized_decode_q4_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+    name = "q4k_rows.hip"
+    with open(os.path.join(ROOT, "quantized_decode_q4_amd", "csrc", name), "rb") as f:
+        h.update(name.encode())
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -107,8 +116,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--kernel-only", default="", help="launch only this part (profiling): "
-                    "gate_up | down | qkv | lmhead | copy (a plain 1 GiB device copy that "
-                    "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+                    "gate_up | down | qkv | lmhead | prefill | copy (a plain 1 GiB device "
+                    "copy that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill FFN leg")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -137,7 +147,7 @@ def main() -> int:
     # ---------------------------------------------------------------- inputs
     t0 = time.perf_counter()
     qkv_host, ffn_host, qkv_dev, ffn_dev = [], [], [], []
-    need_layers = args.kernel_only in ("", "gate_up", "down", "qkv")
+    need_layers = args.kernel_only in ("", "gate_up", "down", "qkv", "prefill")
     for l in range(LAYERS if need_layers else 0):
         c = inputs.qkv(copy=l)
         L = inputs.ffn_layer(l)
@@ -165,6 +175,17 @@ def main() -> int:
     top_val = torch.empty(TOPK, device=dev)
     lm_ws = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(VOCAB, HIDDEN, TOPK))
     GELU = q4k.Q4K_ACT_GELU_TANH
+    do_prefill = not args.no_prefill and args.kernel_only in ("", "prefill")
+    if do_prefill:
+        Xp = [up(inputs.prefill_x(index=l)) for l in range(LAYERS)]
+        Yp = torch.empty((PREFILL_SEQ, HIDDEN), device=dev)
+        p_ws = q4k.workspace(q4k.q4k_ffn_prefill_workspace_bytes(PREFILL_SEQ, HIDDEN, INTER))
+
+    def run_prefill():
+        for l in range(LAYERS):
+            L = ffn_dev[l]
+            q4k.q4k_ffn_prefill(L["Wg"], L["Wu"], L["Wd"], Xp[l], Yp, PREFILL_SEQ, HIDDEN, INTER,
+                                GELU, p_ws)
 
     def run_layers():
         for l in range(LAYERS):
@@ -193,6 +214,7 @@ def main() -> int:
             "qkv": lambda: [q4k.q4k_qkv(c["W"], c["x"], q, k, v, QROWS, KVROWS, HIDDEN)
                             for c in qkv_dev],
             "lmhead": run_lmhead,
+            "prefill": run_prefill,
         }
         fn = parts[args.kernel_only]
         for i in range(args.warmup + args.steps):
@@ -281,6 +303,44 @@ def main() -> int:
     traffic = counters_traffic("gate_up")
     log(f"gate_up: {gu_ms * 1e3:.2f} us/launch, {gu_gbs:.0f} GB/s")
 
+    # ------------------------------------------ prefill FFN (matrix cores)
+    prefill = None
+    if do_prefill:
+        run_prefill()
+        torch.cuda.synchronize()
+        g_pf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pf):
+            run_prefill()
+        torch.cuda.synchronize()
+        g_pf.replay()
+        torch.cuda.synchronize()
+        per_call = []
+        for _ in range(5):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            g_pf.replay()
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            per_call.append(a_ev.elapsed_time(b_ev) / LAYERS)
+        per_call.sort()
+        pf_ms = per_call[len(per_call) // 2]
+        tflops = PREFILL_FLOPS / (pf_ms * 1e-3) / 1e12
+        pf_gbs = PREFILL_BYTES / (pf_ms * 1e-3) / 1e9
+        prefill = {
+            "workload": "gated FFN prefill, 64 tokens x (gate/up 2 x 10240x2560, down 2560x10240), "
+                        "GELU-tanh, Q4_K weights, bf16 MFMA operands, fp32 accumulation; "
+                        "34 layers' weights in rotation",
+            "us_per_call": round(pf_ms * 1e3, 3),
+            "tflops": round(tflops, 2),
+            "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(pf_gbs, 1),
+            "hbm_frac": round(pf_gbs / HBM_PEAK_GBS, 4),
+            "flops_per_call": PREFILL_FLOPS,
+            "algorithmic_bytes_per_call": PREFILL_BYTES,
+        }
+        log(f"prefill FFN: {pf_ms * 1e3:.2f} us/call, {tflops:.0f} TFLOP/s "
+            f"({100 * tflops / BF16_PEAK_TFLOPS:.1f}% of bf16 peak), {pf_gbs:.0f} GB/s")
+
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu:
@@ -330,6 +390,7 @@ def main() -> int:
             "us_per_launch": round(gu_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     print(json.dumps(rec), flush=True)
     return 0

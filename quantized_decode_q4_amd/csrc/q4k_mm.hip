@@ -205,6 +205,14 @@ struct WSlot {
     uint2 sq[B > 0 ? B : 1];                                          //   and 8 quant bytes
 };
 
+// LDS operands of one K-step: the four token tiles (own tiles), this wave's
+// token tile and the shared tiles' weights.
+template <int B>
+struct Ops {
+    bf16x8 xa[4], xw;
+    bf16x8 wb[B > 0 ? B : 1];
+};
+
 template <int NMAT>
 __device__ __forceinline__ const uint8_t *row_ptr(const MmArgs &p, int64_t tile, int nn)
 {
@@ -327,16 +335,30 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
                 Coef k[A > 0 ? A : 1];
 #pragma unroll
                 for (int i = 0; i < A; ++i) k[i] = block_coef(sl.oh[i], c);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    bf16x8 xa[4];
+                // LDS operands of K-step j+1 are requested before K-step j is
+                // dequantised and multiplied, so their latency hides behind that work.
+                const uint8_t *sbase = bbuf + ((b & 1) * B) * 8192;
+                auto read_ops = [&](int j, Ops<B> &o) {
                     if constexpr (A > 0) {
 #pragma unroll
                         for (int tt = 0; tt < 4; ++tt)
-                            xa[tt] = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + tt) * 64 + l) * 16);
-                    } else {
-                        xa[0] = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + wave_u) * 64 + l) * 16);
+                            o.xa[tt] = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + tt) * 64 + l) * 16);
                     }
+                    if constexpr (B > 0) {
+                        // this wave's token tile, for the shared tiles (a second LDS
+                        // read rather than a per-lane select or a branch)
+                        o.xw = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + wave_u) * 64 + l) * 16);
+#pragma unroll
+                        for (int s = 0; s < B; ++s)
+                            o.wb[s] = *reinterpret_cast<const bf16x8 *>(sbase + s * 8192 + (j * 64 + b_pos(n, c, j)) * 16);
+                    }
+                };
+                Ops<B> ops[2];
+                read_ops(0, ops[0]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (j + 1 < 8) read_ops(j + 1, ops[(j + 1) & 1]);
+                    const Ops<B> &o = ops[j & 1];
 #pragma unroll
                     for (int i = 0; i < A; ++i) {
                         const uint4 &qa = (j & 3) < 2 ? sl.oq0[i] : sl.oq1[i];
@@ -345,22 +367,11 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
                                                 : deq8<true>(w0, w1, k[i].a_hi, k[i].b_hi);
 #pragma unroll
                         for (int tt = 0; tt < 4; ++tt)
-                            acc[i][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tt], wb, acc[i][tt], 0, 0, 0);
+                            acc[i][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.xa[tt], wb, acc[i][tt], 0, 0, 0);
                     }
 #pragma unroll
-                    for (int s = 0; s < B; ++s) {
-                        const uint8_t *base = bbuf + ((b & 1) * B + s) * 8192;
-                        const bf16x8 wb = *reinterpret_cast<const bf16x8 *>(base + (j * 64 + b_pos(n, c, j)) * 16);
-                        if constexpr (A > 0) {
-                            // token tile `wave` (uniform): a scalar branch, no operand select
-#pragma unroll
-                            for (int tt = 0; tt < 4; ++tt)
-                                if (tt == wave_u)
-                                    acc_sh[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tt], wb, acc_sh[s], 0, 0, 0);
-                        } else {
-                            acc_sh[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], wb, acc_sh[s], 0, 0, 0);
-                        }
-                    }
+                    for (int s = 0; s < B; ++s)
+                        acc_sh[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.xw, o.wb[s], acc_sh[s], 0, 0, 0);
                 }
                 if constexpr (B > 0) {
                     if (b + 1 < nblk) prep_shared(ring[(u + 1) % kRing], (b + 1) & 1);
