@@ -181,11 +181,9 @@ Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int
 
 Q4K_EXPORT size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq)
 {
-    if (!rows_ok(rows) || !cols_ok(cols) || seq < 0) return 0;
+    if (!rows_ok(rows) || !cols_ok(cols) || seq < 0 || seq > kSeqMax) return 0;
     if (seq < kMfmaMinSeq || rows == 0) return 0;
-    const q4k::MmPlan pl = q4k::mm_plan(rows, cols, seq, 1);
-    return round_up((size_t)q4k::mm_frag_bytes(seq, cols), 256) +
-           round_up((size_t)q4k::mm_partial_bytes(pl, seq, rows, 1), 256);
+    return (size_t)q4k::mm_matmul_workspace(rows, cols, seq);
 }
 
 Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
@@ -205,10 +203,8 @@ Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows,
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
     if (seq >= kMfmaMinSeq) {
-        uint8_t *w8 = (uint8_t *)ws;
-        float *partial = (float *)(w8 + round_up((size_t)q4k::mm_frag_bytes(seq, cols), 256));
-        return hip_status(q4k::launch_matmul_mfma((const uint8_t *)W, X, Y, rows, cols, seq, w8,
-                                                  partial, s));
+        return hip_status(q4k::launch_matmul_mfma((const uint8_t *)W, X, Y, rows, cols, seq,
+                                                  (uint8_t *)ws, s));
     }
     // f32 path: one matvec per token (every token re-reads W).
     for (int64_t t = 0; t < seq; ++t) {
@@ -224,14 +220,8 @@ Q4K_EXPORT size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, i
 {
     if (seq < 0 || !cols_ok(hidden) || !cols_ok(inter)) return 0;
     size_t need = round_up((size_t)inter * 4, 256);
-    if (seq >= kMfmaMinSeq) {
-        const q4k::MmPlan pg = q4k::mm_plan(inter, hidden, seq, 2);
-        const q4k::MmPlan pd = q4k::mm_plan(hidden, inter, seq, 1);
-        const int64_t pa = q4k::mm_partial_bytes(pg, seq, inter, 2);
-        const int64_t pb = q4k::mm_partial_bytes(pd, seq, hidden, 1);
-        const size_t mm = round_up((size_t)q4k::mm_frag_bytes(seq, hidden), 256) +
-                          round_up((size_t)q4k::mm_frag_bytes(seq, inter), 256) +
-                          round_up((size_t)(pa > pb ? pa : pb), 256);
+    if (seq >= kMfmaMinSeq && seq <= kSeqMax) {
+        const size_t mm = (size_t)q4k::mm_ffn_workspace(seq, hidden, inter);
         need = mm > need ? mm : need;
     }
     return need;
@@ -259,12 +249,9 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
     if (seq >= kMfmaMinSeq) {
-        uint8_t *xf = (uint8_t *)ws;
-        uint8_t *hf = xf + round_up((size_t)q4k::mm_frag_bytes(seq, hidden), 256);
-        float *partial = (float *)(hf + round_up((size_t)q4k::mm_frag_bytes(seq, inter), 256));
         return hip_status(q4k::launch_ffn_prefill_mfma((const uint8_t *)Wg, (const uint8_t *)Wu,
                                                        (const uint8_t *)Wd, X, Y, seq, hidden,
-                                                       inter, act, xf, hf, partial, s));
+                                                       inter, act, (uint8_t *)ws, s));
     }
     for (int64_t t = 0; t < seq; ++t) {
         const int st = hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,

@@ -38,29 +38,16 @@ hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, i
                               int64_t cols, int k, uint64_t *cand, int32_t *top_idx,
                               float *top_val, hipStream_t s);
 
-// Matrix-core prefill (q4k_mm.hip). A plan fixes the tiles of 16 weight rows
-// per workgroup (n_t), the K split (S splits of kps super-blocks), the row
-// groups (rg) and the 64-token groups (tg) of one launch.
-struct MmPlan {
-    int n_t, S, kps;
-    int64_t rg, tg;
-};
-// nmat = 2 for the gate/up pair (rows = inter, a tile is 8 rows of each).
-MmPlan mm_plan(int64_t rows, int64_t cols, int64_t seq, int nmat);
-// bf16 activation fragments for seq tokens (padded to 64) of cols values.
-int64_t mm_frag_bytes(int64_t seq, int64_t cols);
-// f32 partial sums of a K-split plan (0 without a split).
-int64_t mm_partial_bytes(const MmPlan &pl, int64_t seq, int64_t rows, int nmat);
-// Y[seq][rows] = X W^T; Xf (mm_frag_bytes) and partial (mm_partial_bytes)
-// are workspace.
+// Matrix-core prefill (q4k_mm.hip), for seq >= 64 tokens. Workspace sizes
+// (bytes) for the current device, and the launches that carve them.
+int64_t mm_matmul_workspace(int64_t rows, int64_t cols, int64_t seq);
+int64_t mm_ffn_workspace(int64_t seq, int64_t hidden, int64_t inter);
+// Y[seq][rows] = X W^T.
 hipError_t launch_matmul_mfma(const uint8_t *W, const float *X, float *Y, int64_t rows,
-                              int64_t cols, int64_t seq, uint8_t *Xf, float *partial,
-                              hipStream_t s);
-// Gated FFN for seq tokens; Xf / Hf fragments of X and H, partial for the
-// larger of the two plans' partial sums.
+                              int64_t cols, int64_t seq, uint8_t *ws, hipStream_t s);
+// Gated FFN for seq tokens: H = act(X Wg^T) * (X Wu^T) (bf16), Y = H Wd^T.
 hipError_t launch_ffn_prefill_mfma(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd,
                                    const float *X, float *Y, int64_t seq, int64_t hidden,
-                                   int64_t inter, int act, uint8_t *Xf, uint8_t *Hf,
-                                   float *partial, hipStream_t s);
+                                   int64_t inter, int act, uint8_t *ws, hipStream_t s);
 
 }  // namespace q4k

@@ -57,42 +57,48 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector: no struct copies
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
 constexpr int kTokGroup = 64;          // tokens per group (four 16-token tiles)
 constexpr int kChunk = 32768;          // bytes of one super-block column of a token group
 constexpr int kXBufs = 3;              // activation chunks in the LDS ring
-constexpr int kRing = 5;               // weight register ring slots (4 blocks in flight)
-constexpr int kComputeThreads = 256;
-constexpr int kThreads = 320;          // + one loader wave
+constexpr int kRing = 5;               // weight register ring slots (4 super-blocks in flight)
+constexpr int kComputeWaves = 8;       // two per SIMD
+constexpr int kComputeThreads = 64 * kComputeWaves;
+constexpr int kThreads = kComputeThreads + 64;   // + one loader wave
 constexpr int kTileBytesPerBlock = 16 * kBlockBytes;
 
-enum MmEpi { MM_EPI_Y = 0, MM_EPI_PARTIAL = 1, MM_EPI_GATED = 2 };
+// A launch plan: tiles of 16 weight rows per workgroup (n_t), the K split (S
+// splits of kps super-blocks), the row groups (rg) and the 64-token groups (tg).
+struct MmPlan {
+    int n_t, S, kps;
+    int64_t rg, tg;
+};
 
 struct MmArgs {
     const uint8_t *W0;     // weights (gate matrix of the pair)
     const uint8_t *W1;     // up matrix of the pair (unused for one matrix)
     const uint8_t *Xf;     // bf16 activation fragments, KB = nb super-blocks per token group
-    void *out;             // MM_EPI_Y: f32 [seq][rows]; MM_EPI_PARTIAL: f32 [S][seq][NMAT*rows];
-                           // MM_EPI_GATED: bf16 fragments of H (KB = out_kb)
+    void *out;             // one matrix: Y f32 [seq][rows]; the pair: H as bf16 fragments (KB = out_kb)
+    float *partial;        // K splits: f32 [S][seq][NMAT*rows]
     int32_t rows;          // rows per matrix
     int32_t nb;            // super-blocks per weight row
     int32_t seq;
     int32_t n_tiles;       // tiles per workgroup (4A + B)
     int32_t S;             // K splits
     int32_t kps;           // super-blocks per split
-    int32_t epi;
     int32_t act;
     int32_t out_kb;
 };
 
+// Gated activations as z * sigmoid(k): GELU-tanh has k = 2 sqrt(2/pi) (z +
+// 0.044715 z^3), since 0.5 z (1 + tanh(y)) = z / (1 + e^(-2y)); SiLU has k = z.
+// One exponential and one reciprocal; the result is rounded to bf16 next.
 __device__ __forceinline__ float act_apply(float z, int act)
 {
-    if (act == 0) {
-        const float c = 0.7978845608028654f;  // sqrt(2/pi)
-        return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
-    }
-    return z / (1.0f + expf(-z));
+    const float k = act == 0 ? 1.5957691216057308f * (z + 0.044715f * z * z * z) : z;
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-k));
 }
 
 // Byte offset of (token, k) in a fragment-major bf16 activation buffer with
@@ -198,18 +204,22 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Weight loads of one super-block, per thread: own tiles (header + the 16
+// quant bytes of this wave's half of the lane's 32-byte group) and shared
+// tiles (header + 4 quant bytes).
 template <int A, int B>
-struct WSlot {
-    uint4 oh[A > 0 ? A : 1], oq0[A > 0 ? A : 1], oq1[A > 0 ? A : 1];   // own tiles: header, quants
-    uint4 sh[B > 0 ? B : 1];                                          // shared tiles: header
-    uint2 sq[B > 0 ? B : 1];                                          //   and 8 quant bytes
+struct Slot {
+    uint4 oh[A > 0 ? A : 1], oq[A > 0 ? A : 1];
+    uint4 sh[B > 0 ? B : 1];
+    uint32_t sq[B > 0 ? B : 1];
 };
 
-// LDS operands of one K-step: the four token tiles (own tiles), this wave's
-// token tile and the shared tiles' weights.
+// LDS operands of one K-step: the four token tiles, rotated so that xa[0] is
+// this SIMD's own token tile (the shared tiles' operand), and the shared
+// tiles' weights.
 template <int B>
 struct Ops {
-    bf16x8 xa[4], xw;
+    bf16x8 xa[4];
     bf16x8 wb[B > 0 ? B : 1];
 };
 
@@ -230,6 +240,27 @@ __device__ __forceinline__ const uint8_t *row_ptr(const MmArgs &p, int64_t tile,
     return base + row * (int64_t)p.nb * kBlockBytes;
 }
 
+// Four weights from one quant word: low (HI = false) or high nibbles of bytes
+// 0..3, rounded to bf16, as two words.
+template <bool HI>
+__device__ __forceinline__ uint2 deq4(uint32_t w, float a, float b)
+{
+    const uint32_t u = and_opaque(w, HI ? 0xF0F0F0F0u : 0x0F0F0F0Fu);
+    uint2 r;
+    r.x = pack_bf16(fmaf(a, (float)(u & 0xFFu), b), fmaf(a, (float)((u >> 8) & 0xFFu), b));
+    r.y = pack_bf16(fmaf(a, (float)((u >> 16) & 0xFFu), b), fmaf(a, (float)(u >> 24), b));
+    return r;
+}
+
+// The matrix-core kernel. Waves 0..7 compute: SIMD s = wave % 4 runs waves s
+// and s + 4, which split every super-block's eight K-steps by quant-byte half
+// (half h covers bytes 16h..16h+15 of each 32-byte group: K-steps 2h, 2h+1 of
+// the low nibbles and 4+2h, 5+2h of the high nibbles), so the two waves of a
+// SIMD dequantise disjoint weights; their partial sums are added at the end.
+// Wave 8 is the loader: it copies the activation chunks of the next
+// super-blocks into a 3-deep LDS ring with LDS-DMA loads, on a wait counter
+// of its own, so the compute waves' weight prefetch (a register ring of
+// kRing - 1 super-blocks) never waits on it. One barrier per super-block.
 template <int NMAT, int A, int B>
 __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
 {
@@ -245,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
     const int t = threadIdx.x;
     const int wave = t >> 6, l = t & 63;
 
-    if (wave == 4) {
+    if (wave == kComputeWaves) {
         // Loader: chunk b (activations of super-block kb0 + b) -> xbuf[b % 3].
         const uint8_t *src = p.Xf + ((int64_t)tg * p.nb + kb0) * kChunk + l * 16;
         auto issue = [&](int b) {
@@ -263,52 +294,56 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
             barrier_lds();
             if (b + 2 < nblk) issue(b + 2);   // into the buffer chunk b-1 used
         }
+        barrier_lds();   // the compute waves' two barriers of the pair reduction
+        barrier_lds();
         return;
     }
 
     const int n = l & 15, c = l >> 4;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int ns = t >> 4, q = t & 15;       // shared-tile dequant: row ns, quant piece q
+    const int simd = wave & 3, half = wave >> 2;
+    const int ns = t >> 5, q4 = t & 31;      // shared-tile dequant: row ns, quant word q4
     const uint8_t *rp_own[A > 0 ? A : 1];
     const uint8_t *rp_sh[B > 0 ? B : 1];
 #pragma unroll
-    for (int i = 0; i < A; ++i) rp_own[i] = row_ptr<NMAT>(p, tile0 + wave * A + i, n);
+    for (int i = 0; i < A; ++i) rp_own[i] = row_ptr<NMAT>(p, tile0 + simd * A + i, n);
 #pragma unroll
     for (int s = 0; s < B; ++s) rp_sh[s] = row_ptr<NMAT>(p, tile0 + 4 * A + s, ns);
 
-    WSlot<A, B> ring[kRing];
-    auto load = [&](WSlot<A, B> &sl, int b) {
+    Slot<A, B> ring[kRing];
+    auto load = [&](Slot<A, B> &sl, int b) {
         const int64_t off = (int64_t)(kb0 + min(b, nblk - 1)) * kBlockBytes;
 #pragma unroll
         for (int i = 0; i < A; ++i) {
             const uint8_t *r = rp_own[i] + off;
             sl.oh[i] = *reinterpret_cast<const uint4 *>(r);
-            sl.oq0[i] = *reinterpret_cast<const uint4 *>(r + 16 + 32 * c);
-            sl.oq1[i] = *reinterpret_cast<const uint4 *>(r + 32 + 32 * c);
+            sl.oq[i] = *reinterpret_cast<const uint4 *>(r + 16 + 32 * c + 16 * half);
         }
 #pragma unroll
         for (int s = 0; s < B; ++s) {
             const uint8_t *r = rp_sh[s] + off;
             sl.sh[s] = *reinterpret_cast<const uint4 *>(r);
-            sl.sq[s] = *reinterpret_cast<const uint2 *>(r + 16 + 8 * q);
+            sl.sq[s] = *reinterpret_cast<const uint32_t *>(r + 16 + 4 * q4);
         }
     };
-    // Shared tiles of one block -> LDS operand buffer `buf`.
-    auto prep_shared = [&](const WSlot<A, B> &sl, int buf) {
+    // Shared tiles of one block -> LDS operand buffer `buf`. Thread (ns, q4)
+    // owns quant bytes 4q4..4q4+3 of a shared row: group g = q4/8, K-step
+    // (q4%8)/2 (low nibbles; +4 for the high ones), elements 4(q4%2)..+3 of
+    // that slot.
+    auto stage = [&](const Slot<A, B> &sl, int buf) {
 #pragma unroll
         for (int s = 0; s < B; ++s) {
-            const int g = q >> 2, jl = q & 3;
+            const int g = q4 >> 3, jl = (q4 & 7) >> 1, sub = q4 & 1;
             const Coef k = block_coef(sl.sh[s], g);
-            const bf16x8 lo = deq8<false>(sl.sq[s].x, sl.sq[s].y, k.a_lo, k.b_lo);
-            const bf16x8 hi = deq8<true>(sl.sq[s].x, sl.sq[s].y, k.a_hi, k.b_hi);
-            uint8_t *base = bbuf + (buf * B + s) * 8192;
-            *reinterpret_cast<bf16x8 *>(base + (jl * 64 + b_pos(ns, g, jl)) * 16) = lo;
-            *reinterpret_cast<bf16x8 *>(base + ((jl + 4) * 64 + b_pos(ns, g, jl + 4)) * 16) = hi;
+            uint8_t *base = bbuf + (buf * B + s) * 8192 + 8 * sub;
+            *reinterpret_cast<uint2 *>(base + (jl * 64 + b_pos(ns, g, jl)) * 16) =
+                deq4<false>(sl.sq[s], k.a_lo, k.b_lo);
+            *reinterpret_cast<uint2 *>(base + ((jl + 4) * 64 + b_pos(ns, g, jl + 4)) * 16) =
+                deq4<true>(sl.sq[s], k.a_hi, k.b_hi);
         }
     };
 
-    f32x4 acc[A > 0 ? A : 1][4];
-    f32x4 acc_sh[B > 0 ? B : 1];
+    f32x4 acc[A > 0 ? A : 1][4];     // own tile i, token tile (simd + tt) % 4
+    f32x4 acc_sh[B > 0 ? B : 1];     // shared tile s, token tile simd
 #pragma unroll
     for (int i = 0; i < A; ++i)
 #pragma unroll
@@ -321,33 +356,36 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
     // Keep all prologue loads ahead of the first wait (the scheduler would
     // otherwise issue blocks 1.. only after block 0 has arrived).
     asm volatile("" ::: "memory");
-    if constexpr (B > 0) prep_shared(ring[0], 0);
+    if constexpr (B > 0) stage(ring[0], 0);
 
     for (int b0 = 0; b0 < niter; b0 += kRing) {
 #pragma unroll
         for (int u = 0; u < kRing; ++u) {
             const int b = b0 + u;
-            barrier_lds();   // chunk b and the shared operands of block b are in LDS
+            barrier_lds();   // block b's activations and shared operands are in LDS
             load(ring[(u + kRing - 1) % kRing], b + kRing - 1);
             if (b < nblk) {
                 const uint8_t *xb = xbuf + (b % kXBufs) * kChunk;
-                const WSlot<A, B> &sl = ring[u];
+                const uint8_t *sbase = bbuf + ((b & 1) * B) * 8192;
+                const Slot<A, B> &sl = ring[u];
                 Coef k[A > 0 ? A : 1];
 #pragma unroll
                 for (int i = 0; i < A; ++i) k[i] = block_coef(sl.oh[i], c);
-                // LDS operands of K-step j+1 are requested before K-step j is
-                // dequantised and multiplied, so their latency hides behind that work.
-                const uint8_t *sbase = bbuf + ((b & 1) * B) * 8192;
-                auto read_ops = [&](int j, Ops<B> &o) {
+                // this wave's K-steps: jj = 0, 1 low nibbles, 2, 3 high nibbles
+                auto kstep = [&](int jj) { return (jj < 2 ? 0 : 4) + 2 * half + (jj & 1); };
+                // LDS operands of the next K-step are requested before the
+                // current one is dequantised and multiplied.
+                auto read_ops = [&](int jj, Ops<B> &o) {
+                    const int j = kstep(jj);
                     if constexpr (A > 0) {
 #pragma unroll
                         for (int tt = 0; tt < 4; ++tt)
-                            o.xa[tt] = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + tt) * 64 + l) * 16);
+                            o.xa[tt] = *reinterpret_cast<const bf16x8 *>(
+                                xb + ((j * 4 + ((simd + tt) & 3)) * 64 + l) * 16);
+                    } else {
+                        o.xa[0] = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + simd) * 64 + l) * 16);
                     }
                     if constexpr (B > 0) {
-                        // this wave's token tile, for the shared tiles (a second LDS
-                        // read rather than a per-lane select or a branch)
-                        o.xw = *reinterpret_cast<const bf16x8 *>(xb + ((j * 4 + wave_u) * 64 + l) * 16);
 #pragma unroll
                         for (int s = 0; s < B; ++s)
                             o.wb[s] = *reinterpret_cast<const bf16x8 *>(sbase + s * 8192 + (j * 64 + b_pos(n, c, j)) * 16);
@@ -356,47 +394,94 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
                 Ops<B> ops[2];
                 read_ops(0, ops[0]);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (j + 1 < 8) read_ops(j + 1, ops[(j + 1) & 1]);
-                    const Ops<B> &o = ops[j & 1];
+                for (int jj = 0; jj < 4; ++jj) {
+                    if (jj + 1 < 4) read_ops(jj + 1, ops[(jj + 1) & 1]);
+                    const Ops<B> &o = ops[jj & 1];
 #pragma unroll
                     for (int i = 0; i < A; ++i) {
-                        const uint4 &qa = (j & 3) < 2 ? sl.oq0[i] : sl.oq1[i];
-                        const uint32_t w0 = (j & 1) ? qa.z : qa.x, w1 = (j & 1) ? qa.w : qa.y;
-                        const bf16x8 wb = j < 4 ? deq8<false>(w0, w1, k[i].a_lo, k[i].b_lo)
-                                                : deq8<true>(w0, w1, k[i].a_hi, k[i].b_hi);
+                        const uint4 &qa = sl.oq[i];
+                        const uint32_t w0 = (jj & 1) ? qa.z : qa.x, w1 = (jj & 1) ? qa.w : qa.y;
+                        const bf16x8 wb = jj < 2 ? deq8<false>(w0, w1, k[i].a_lo, k[i].b_lo)
+                                                 : deq8<true>(w0, w1, k[i].a_hi, k[i].b_hi);
 #pragma unroll
                         for (int tt = 0; tt < 4; ++tt)
                             acc[i][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.xa[tt], wb, acc[i][tt], 0, 0, 0);
                     }
 #pragma unroll
                     for (int s = 0; s < B; ++s)
-                        acc_sh[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.xw, o.wb[s], acc_sh[s], 0, 0, 0);
+                        acc_sh[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.xa[0], o.wb[s], acc_sh[s], 0, 0, 0);
                 }
                 if constexpr (B > 0) {
-                    if (b + 1 < nblk) prep_shared(ring[(u + 1) % kRing], (b + 1) & 1);
+                    if (b + 1 < nblk) stage(ring[(u + 1) % kRing], (b + 1) & 1);
                 }
             }
         }
     }
 
-    // ---- epilogue ----
-    const int64_t tok_base = tg * kTokGroup;
-    auto store = [&](f32x4 v, int64_t tile, int64_t tok0) {
-        // lane (n, c), register r: token tok0 + 4c + r, tile row n
+    // ---- the two halves of each SIMD add up (through LDS, reusing xbuf) ----
+    constexpr int NACC = 16 * A + 4 * B;
+    float *red = reinterpret_cast<float *>(xbuf) + simd * NACC * 64 + l;
+    barrier_lds();                                  // everyone is done with xbuf
+    if (half == 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t token = tok0 + 4 * c + r;
-            const float val = v[r];
-            if (p.epi == MM_EPI_GATED) {
-                const float other = __int_as_float(
-                    __builtin_amdgcn_update_dpp(0, __float_as_int(val), 0x128, 0xF, 0xF, false));
-                const int64_t irow = 8 * tile + n;
-                if (n < 8 && irow < p.rows) {
-                    const float h = act_apply(val, p.act) * other;
-                    *reinterpret_cast<__bf16 *>((uint8_t *)p.out + frag_offset(token, irow, p.out_kb)) = (__bf16)h;
+        for (int i = 0; i < A; ++i)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[((i * 4 + tt) * 4 + r) * 64] = acc[i][tt][r];
+#pragma unroll
+        for (int s = 0; s < B; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(16 * A + 4 * s + r) * 64] = acc_sh[s][r];
+    }
+    barrier_lds();
+    if (half == 1) return;
+#pragma unroll
+    for (int i = 0; i < A; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][tt][r] += red[((i * 4 + tt) * 4 + r) * 64];
+#pragma unroll
+    for (int s = 0; s < B; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_sh[s][r] += red[(16 * A + 4 * s + r) * 64];
+
+    // ---- epilogue: lane (n, c), register r -> token tok0 + 4c + r, tile row n ----
+    const bool split = p.S > 1;
+    const int64_t tok_base = tg * kTokGroup;
+    auto store = [&](f32x4 v, int64_t tile, int ttile) {
+        const int64_t tok0 = tok_base + 16 * ttile;
+        if (NMAT == 2 && !split) {
+            // gated activation: lanes n < 8 hold the gate rows, n >= 8 the up
+            // rows; a row rotation by 8 pairs them. Lanes n < 8 finish
+            // registers 0, 1, lanes n >= 8 registers 2, 3.
+            float other[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                other[r] = __int_as_float(
+                    __builtin_amdgcn_update_dpp(0, __float_as_int(v[r]), 0x128, 0xF, 0xF, false));
+            const int64_t irow = 8 * tile + (n & 7);
+            if (irow < p.rows) {
+                const int64_t kb = irow >> 8;
+                const int e = (int)irow & 255, cc = e >> 6, rr = e & 63;
+                const int j = ((rr >> 5) << 2) | ((rr & 31) >> 3), ii = rr & 7;
+                // fragment offset of (tok0 + 4c, irow); + 16 bytes per token
+                uint8_t *hb = (uint8_t *)p.out +
+                              ((((tg * p.out_kb + kb) * 8 + j) * 4 + ttile) * 64 + 4 * c + 16 * cc) * 16 + 2 * ii;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int r = (n < 8 ? 0 : 2) + h2;
+                    const float g = n < 8 ? v[r] : other[r];
+                    const float u = n < 8 ? other[r] : v[r];
+                    *reinterpret_cast<__bf16 *>(hb + r * 16) = (__bf16)(act_apply(g, p.act) * u);
                 }
-            } else if (token < p.seq) {
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t token = tok0 + 4 * c + r;
+                if (token >= p.seq) continue;
                 int64_t col, ncols;
                 if (NMAT == 1) {
                     col = 16 * tile + n;
@@ -408,32 +493,29 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
                     col = n < 8 ? irow : (int64_t)p.rows + irow;
                     ncols = 2 * (int64_t)p.rows;
                 }
-                float *o = (float *)p.out;
-                if (p.epi == MM_EPI_PARTIAL) o += (int64_t)sp * p.seq * ncols;
-                o[token * ncols + col] = val;
+                float *o = split ? p.partial + (int64_t)sp * p.seq * ncols : (float *)p.out;
+                o[token * ncols + col] = v[r];
             }
         }
     };
 #pragma unroll
     for (int i = 0; i < A; ++i)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) store(acc[i][tt], tile0 + wave * A + i, tok_base + 16 * tt);
+        for (int tt = 0; tt < 4; ++tt) store(acc[i][tt], tile0 + simd * A + i, (simd + tt) & 3);
 #pragma unroll
-    for (int s = 0; s < B; ++s) store(acc_sh[s], tile0 + 4 * A + s, tok_base + 16 * wave);
+    for (int s = 0; s < B; ++s) store(acc_sh[s], tile0 + 4 * A + s, simd);
 }
 
-// f32 activations [seq][cols] -> bf16 fragments (zeros for padding tokens).
+// f32 activations [seq][cols] -> bf16 fragments; zeros for the padding
+// tokens of the last group. Thread = 8 consecutive values of one token (reads
+// are row-contiguous), written to their 16-byte fragment piece.
 __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *X, uint8_t *Xf, int64_t seq,
-                                                         int64_t cols, int64_t pieces)
+                                                         int64_t seq_pad, int64_t cols)
 {
-    const int64_t pc = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (pc >= pieces) return;
-    const int64_t KB = cols >> 8;
-    const int lane = (int)pc & 63, tt = (int)(pc >> 6) & 3, j = (int)(pc >> 8) & 7;
-    const int64_t rest = pc >> 11, kb = rest % KB, tg = rest / KB;
-    const int64_t token = tg * kTokGroup + 16 * tt + (lane & 15);
-    const int c = lane >> 4;
-    const int64_t k0 = kb * 256 + 64 * c + 32 * (j >> 2) + 8 * (j & 3);
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t k8n = cols >> 3;
+    if (idx >= seq_pad * k8n) return;
+    const int64_t token = idx / k8n, k0 = (idx % k8n) * 8;
     bf16x8 v;
     if (token < seq) {
         const float4 a = *reinterpret_cast<const float4 *>(X + token * cols + k0);
@@ -444,10 +526,10 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *X, uint8_t 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
     }
-    *reinterpret_cast<bf16x8 *>(Xf + pc * 16) = v;
+    *reinterpret_cast<bf16x8 *>(Xf + frag_offset(token, k0, cols >> 8)) = v;
 }
 
-// Y[t][i] = sum_s P[s][t][i], s in order.
+// K splits: Y[t][i] = sum_s P[s][t][i], s in order.
 __global__ __launch_bounds__(256) void reduce_y_kernel(const float *P, float *Y, int64_t n, int S)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -457,8 +539,8 @@ __global__ __launch_bounds__(256) void reduce_y_kernel(const float *P, float *Y,
     Y[i] = acc;
 }
 
-// Gate/up partials P[s][t][0..2 inter) -> H = act(G) * U as bf16 fragments
-// for all tokens of the padded groups (zeros past seq).
+// K splits of the gate/up pair: P[s][t][0..2 inter) -> H = act(G) * U as bf16
+// fragments for every token of the padded groups (zeros past seq).
 __global__ __launch_bounds__(256) void reduce_gated_kernel(const float *P, uint8_t *Hf, int64_t seq,
                                                            int64_t seq_pad, int64_t inter, int S,
                                                            int act)
@@ -496,7 +578,7 @@ int device_cus_mm()
     return cache[dev];
 }
 
-constexpr int kMaxTilesPerWg = 8;
+constexpr int kMaxTilesPerWg = 6;   // 7 and 8 tiles spill registers
 
 // Tiles per workgroup and K split for T tiles of nb super-blocks and TG token
 // groups: minimise the per-CU weight stream of the slowest round plus a charge
@@ -518,8 +600,13 @@ MmPlan plan_for(int64_t T, int nb, int64_t seq, int64_t rows_out, int cus)
         const int64_t rg = (T + n_t - 1) / n_t;
         const int64_t wgs = rg * S * TG;
         const int64_t rounds = (wgs + cus - 1) / cus;
-        double cost = (double)rounds * (double)n_t * kps * kTileBytesPerBlock * cus;
-        if (S > 1) cost += 0.35 * (double)S * (double)seq * (double)rows_out * 8.0;
+        // per-CU bytes of the slowest round: weights from HBM, plus the
+        // activation chunks (32 KB per super-block and token group, from L2,
+        // charged at half weight)
+        double cost = (double)rounds * (double)kps * ((double)n_t * kTileBytesPerBlock + 0.5 * kChunk) * cus;
+        // a split writes and re-reads partial sums and costs a second kernel
+        // (about 3 us of launch and latency, charged as bytes at 6 TB/s)
+        if (S > 1) cost += 0.35 * (double)S * (double)seq * (double)rows_out * 8.0 + 18e6;
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best.n_t = (int)n_t;
@@ -558,65 +645,88 @@ hipError_t launch_mm(const MmArgs &a, const MmPlan &pl, hipStream_t s)
 
 hipError_t launch_x_to_frag(const float *X, uint8_t *Xf, int64_t seq, int64_t cols, hipStream_t s)
 {
-    const int64_t TG = (seq + kTokGroup - 1) / kTokGroup;
-    const int64_t pieces = TG * (cols / 256) * 2048;
-    hipLaunchKernelGGL(x_to_frag_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s,
-                       X, Xf, seq, cols, pieces);
+    const int64_t seq_pad = (seq + kTokGroup - 1) / kTokGroup * kTokGroup;
+    const int64_t n = seq_pad * (cols / 8);
+    hipLaunchKernelGGL(x_to_frag_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, X, Xf,
+                       seq, seq_pad, cols);
     return hipGetLastError();
 }
 
-}  // namespace
+int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+int64_t partial_bytes(const MmPlan &pl, int64_t seq, int64_t rows, int nmat)
+{
+    return pl.S > 1 ? (int64_t)pl.S * seq * rows * nmat * 4 : 0;
+}
 
-MmPlan mm_plan(int64_t rows, int64_t cols, int64_t seq, int nmat)
+MmPlan plan_of(int64_t rows, int64_t cols, int64_t seq, int nmat)
 {
     const int64_t T = nmat == 1 ? (rows + 15) / 16 : (rows + 7) / 8;
     return plan_for(T, (int)(cols / 256), seq, rows * nmat, device_cus_mm());
 }
 
-int64_t mm_frag_bytes(int64_t seq, int64_t cols)
+int64_t frag_bytes(int64_t seq, int64_t cols)
 {
     return (seq + kTokGroup - 1) / kTokGroup * kTokGroup * cols * 2;
 }
 
-int64_t mm_partial_bytes(const MmPlan &pl, int64_t seq, int64_t rows, int nmat)
+hipError_t launch_reduce_y(const float *P, float *Y, int64_t n, int S, hipStream_t s)
 {
-    return pl.S > 1 ? (int64_t)pl.S * seq * rows * nmat * 4 : 0;
+    hipLaunchKernelGGL(reduce_y_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, Y, n, S);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Workspace of the matrix product: activation fragments | partial sums of a
+// K split (each piece 256-byte aligned).
+int64_t mm_matmul_workspace(int64_t rows, int64_t cols, int64_t seq)
+{
+    const MmPlan pl = plan_of(rows, cols, seq, 1);
+    return up256(frag_bytes(seq, cols)) + up256(partial_bytes(pl, seq, rows, 1));
+}
+
+// Workspace of the gated FFN: X fragments | H fragments | partial sums (the
+// larger stage's; the stages run in order).
+int64_t mm_ffn_workspace(int64_t seq, int64_t hidden, int64_t inter)
+{
+    const MmPlan pg = plan_of(inter, hidden, seq, 2), pd = plan_of(hidden, inter, seq, 1);
+    const int64_t pa = partial_bytes(pg, seq, inter, 2), pb = partial_bytes(pd, seq, hidden, 1);
+    return up256(frag_bytes(seq, hidden)) + up256(frag_bytes(seq, inter)) + up256(pa > pb ? pa : pb);
 }
 
 hipError_t launch_matmul_mfma(const uint8_t *W, const float *X, float *Y, int64_t rows,
-                              int64_t cols, int64_t seq, uint8_t *Xf, float *partial,
-                              hipStream_t s)
+                              int64_t cols, int64_t seq, uint8_t *ws, hipStream_t s)
 {
-    const MmPlan pl = mm_plan(rows, cols, seq, 1);
+    const MmPlan pl = plan_of(rows, cols, seq, 1);
+    uint8_t *Xf = ws;
+    float *partial = (float *)(Xf + up256(frag_bytes(seq, cols)));
     hipError_t e = launch_x_to_frag(X, Xf, seq, cols, s);
     if (e != hipSuccess) return e;
     MmArgs a{};
     a.W0 = W;
     a.W1 = W;
     a.Xf = Xf;
+    a.out = Y;
+    a.partial = partial;
     a.rows = (int32_t)rows;
     a.nb = (int32_t)(cols / 256);
     a.seq = (int32_t)seq;
     a.n_tiles = pl.n_t;
     a.S = pl.S;
     a.kps = pl.kps;
-    a.epi = pl.S > 1 ? MM_EPI_PARTIAL : MM_EPI_Y;
-    a.out = pl.S > 1 ? (void *)partial : (void *)Y;
     e = launch_mm<1>(a, pl, s);
     if (e != hipSuccess || pl.S == 1) return e;
-    const int64_t nout = seq * rows;
-    hipLaunchKernelGGL(reduce_y_kernel, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s,
-                       partial, Y, nout, pl.S);
-    return hipGetLastError();
+    return launch_reduce_y(partial, Y, seq * rows, pl.S, s);
 }
 
 hipError_t launch_ffn_prefill_mfma(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd,
                                    const float *X, float *Y, int64_t seq, int64_t hidden,
-                                   int64_t inter, int act, uint8_t *Xf, uint8_t *Hf,
-                                   float *partial, hipStream_t s)
+                                   int64_t inter, int act, uint8_t *ws, hipStream_t s)
 {
-    const MmPlan pg = mm_plan(inter, hidden, seq, 2);
-    const MmPlan pd = mm_plan(hidden, inter, seq, 1);
+    const MmPlan pg = plan_of(inter, hidden, seq, 2), pd = plan_of(hidden, inter, seq, 1);
+    uint8_t *Xf = ws;
+    uint8_t *Hf = Xf + up256(frag_bytes(seq, hidden));
+    float *partial = (float *)(Hf + up256(frag_bytes(seq, inter)));
     hipError_t e = launch_x_to_frag(X, Xf, seq, hidden, s);
     if (e != hipSuccess) return e;
 
@@ -624,6 +734,8 @@ hipError_t launch_ffn_prefill_mfma(const uint8_t *Wg, const uint8_t *Wu, const u
     a.W0 = Wg;
     a.W1 = Wu;
     a.Xf = Xf;
+    a.out = Hf;
+    a.partial = partial;
     a.rows = (int32_t)inter;
     a.nb = (int32_t)(hidden / 256);
     a.seq = (int32_t)seq;
@@ -632,13 +744,10 @@ hipError_t launch_ffn_prefill_mfma(const uint8_t *Wg, const uint8_t *Wu, const u
     a.kps = pg.kps;
     a.act = act;
     a.out_kb = (int32_t)(inter / 256);
-    a.epi = pg.S > 1 ? MM_EPI_PARTIAL : MM_EPI_GATED;
-    a.out = pg.S > 1 ? (void *)partial : (void *)Hf;
     e = launch_mm<2>(a, pg, s);
     if (e != hipSuccess) return e;
     if (pg.S > 1) {
-        const int64_t seq_pad = pg.tg * kTokGroup;
-        const int64_t n = seq_pad * inter;
+        const int64_t seq_pad = pg.tg * kTokGroup, n = seq_pad * inter;
         hipLaunchKernelGGL(reduce_gated_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            partial, Hf, seq, seq_pad, inter, pg.S, act);
         e = hipGetLastError();
@@ -649,20 +758,17 @@ hipError_t launch_ffn_prefill_mfma(const uint8_t *Wg, const uint8_t *Wu, const u
     d.W0 = Wd;
     d.W1 = Wd;
     d.Xf = Hf;
+    d.out = Y;
+    d.partial = partial;
     d.rows = (int32_t)hidden;
     d.nb = (int32_t)(inter / 256);
     d.seq = (int32_t)seq;
     d.n_tiles = pd.n_t;
     d.S = pd.S;
     d.kps = pd.kps;
-    d.epi = pd.S > 1 ? MM_EPI_PARTIAL : MM_EPI_Y;
-    d.out = pd.S > 1 ? (void *)partial : (void *)Y;
     e = launch_mm<1>(d, pd, s);
     if (e != hipSuccess || pd.S == 1) return e;
-    const int64_t nout = seq * hidden;
-    hipLaunchKernelGGL(reduce_y_kernel, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s,
-                       partial, Y, nout, pd.S);
-    return hipGetLastError();
+    return launch_reduce_y(partial, Y, seq * hidden, pd.S, s);
 }
 
 }  // namespace q4k
