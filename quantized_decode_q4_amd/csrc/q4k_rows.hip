@@ -54,6 +54,9 @@
 #ifndef Q4K_STORE_WGS_PER_CU
 #define Q4K_STORE_WGS_PER_CU 1
 #endif
+#ifndef Q4K_STORE_F32_SWEEPS
+#define Q4K_STORE_F32_SWEEPS 2      // sweeps per workgroup up to which matvec uses f32 activations
+#endif
 #ifndef Q4K_GATE_UP_D
 #define Q4K_GATE_UP_D 1
 #endif
@@ -824,8 +827,14 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     a.split0 = split0;
     a.split1 = split1;
     const Shape sh = pick_shape(cols);
-    return launch_rows_bfp<1, EPI_STORE, Q4K_STORE_D>(a, sh.rps, sh.threads,
-                                                      grid_for(rows, cols, sh, Q4K_STORE_WGS_PER_CU), s);
+    const int64_t nwg = grid_for(rows, cols, sh, Q4K_STORE_WGS_PER_CU);
+#if Q4K_STORE_F32_SWEEPS > 0
+    // few sweeps per workgroup: f32 activations, no shared conversion step
+    const int64_t sweeps = (rows + sh.rps - 1) / sh.rps;
+    if (sweeps <= (int64_t)Q4K_STORE_F32_SWEEPS * nwg)
+        return launch_rows<1, EPI_STORE, XS_F32, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s);
+#endif
+    return launch_rows_bfp<1, EPI_STORE, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s);
 }
 
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
