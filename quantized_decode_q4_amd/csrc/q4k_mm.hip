@@ -63,7 +63,8 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 constexpr int kTokGroup = 64;          // tokens per group (four 16-token tiles)
 constexpr int kChunk = 32768;          // bytes of one super-block column of a token group
 constexpr int kXBufs = 3;              // activation chunks in the LDS ring
-constexpr int kRing = 5;               // weight register ring slots (4 super-blocks in flight)
+constexpr int kRing = 3;               // weight register ring slots (2 super-blocks in flight; deeper
+                                       // rings measured slower: the extra loads congest the CU)
 constexpr int kComputeWaves = 8;       // two per SIMD
 constexpr int kComputeThreads = 64 * kComputeWaves;
 constexpr int kThreads = kComputeThreads + 64;   // + one loader wave
