@@ -8,7 +8,8 @@ before timing; 34 distinct layers exceed the 256 MB Infinity Cache, so each
 step streams its weights from HBM. Steps are replayed from HIP graphs captured
 once (launch-bound inner loop); the eager launch rate is reported beside it.
 
-Beside the step, the 64-token prefill FFN on the same 34 layers' weights (the
+Beside the step: the full Q4_K sequence of a layer (QKV, the attention output
+projection 2560 x 2048, FFN) over the 34 layers, and the 64-token prefill FFN on the same 34 layers' weights (the
 matrix-core path) is timed per call and reported with its MFMA utilisation.
 
 Prints ONE JSON line (see the fields at the end of main()).
@@ -46,6 +47,8 @@ QKV_BYTES = wbytes(QROWS + 2 * KVROWS, HIDDEN) + HIDDEN * 4 + (QROWS + 2 * KVROW
 GATE_UP_BYTES = 2 * wbytes(INTER, HIDDEN) + HIDDEN * 4 + INTER * 4
 DOWN_BYTES = wbytes(HIDDEN, INTER) + INTER * 4 + HIDDEN * 4
 LAYER_BYTES = QKV_BYTES + GATE_UP_BYTES + DOWN_BYTES
+# The attention output projection (2560 x 2048), timed in the full-layer sequence
+O_BYTES = wbytes(HIDDEN, QROWS) + QROWS * 4 + HIDDEN * 4
 LMHEAD_BYTES = wbytes(VOCAB, HIDDEN) + HIDDEN * 4 + VOCAB * 4 + TOPK * 8
 STEP_BYTES = LAYERS * LAYER_BYTES + LMHEAD_BYTES
 # Prefill FFN, 64 tokens: weights once, X in, Y out; 2 flops per weight per token.
@@ -146,13 +149,16 @@ def main() -> int:
 
     # ---------------------------------------------------------------- inputs
     t0 = time.perf_counter()
-    qkv_host, ffn_host, qkv_dev, ffn_dev = [], [], [], []
+    qkv_host, ffn_host, qkv_dev, ffn_dev, o_dev = [], [], [], [], []
     need_layers = args.kernel_only in ("", "gate_up", "down", "qkv", "prefill")
     for l in range(LAYERS if need_layers else 0):
         c = inputs.qkv(copy=l)
         L = inputs.ffn_layer(l)
         qkv_dev.append({"W": up(c["W"]), "x": up(c["x"])})
         ffn_dev.append({k: up(L[k]) for k in ("Wg", "Wu", "Wd", "x")})
+        if not args.kernel_only:
+            o = inputs.o_proj(l)
+            o_dev.append({"W": up(o["W"]), "x": up(o["x"])})
         if not args.no_cpu:
             qkv_host.append(c)
             ffn_host.append(L)
@@ -166,6 +172,7 @@ def main() -> int:
         f"({time.perf_counter() - t0:.1f}s)")
 
     q = torch.empty(QROWS, device=dev)
+    yo = torch.empty(HIDDEN, device=dev)
     k = torch.empty(KVROWS, device=dev)
     v = torch.empty(KVROWS, device=dev)
     y = torch.empty(HIDDEN, device=dev)
@@ -191,6 +198,14 @@ def main() -> int:
         for l in range(LAYERS):
             c, L = qkv_dev[l], ffn_dev[l]
             q4k.q4k_qkv(c["W"], c["x"], q, k, v, QROWS, KVROWS, HIDDEN)
+            q4k.q4k_ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], y, HIDDEN, INTER, GELU, h)
+
+    def run_full_layers():
+        # the whole Q4_K sequence of a layer: QKV, attention output projection, FFN
+        for l in range(LAYERS):
+            c, o, L = qkv_dev[l], o_dev[l], ffn_dev[l]
+            q4k.q4k_qkv(c["W"], c["x"], q, k, v, QROWS, KVROWS, HIDDEN)
+            q4k.q4k_matvec(o["W"], o["x"], yo, HIDDEN, QROWS)
             q4k.q4k_ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], y, HIDDEN, INTER, GELU, h)
 
     def run_lmhead():
@@ -303,6 +318,25 @@ def main() -> int:
     traffic = counters_traffic("gate_up")
     log(f"gate_up: {gu_ms * 1e3:.2f} us/launch, {gu_gbs:.0f} GB/s")
 
+    # ------------------------- full layer sequence (QKV, O projection, FFN)
+    g_full = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_full):
+        run_full_layers()
+    torch.cuda.synchronize()
+    g_full.replay()
+    torch.cuda.synchronize()
+    full_ms = []
+    for _ in range(5):
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        g_full.replay()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        full_ms.append(a_ev.elapsed_time(b_ev))
+    full_ms.sort()
+    us_full_layer = full_ms[len(full_ms) // 2] * 1e3 / LAYERS
+    log(f"full layer (QKV + O + FFN): {us_full_layer:.2f} us")
+
     # ------------------------------------------ prefill FFN (matrix cores)
     prefill = None
     if do_prefill:
@@ -375,6 +409,8 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "us_per_decode_layer": round(us_per_layer, 3),
         "decode_layer_gbs": round(LAYER_BYTES / (us_per_layer * 1e-6) / 1e9, 1),
+        "us_per_full_layer": round(us_full_layer, 3),
+        "full_layer_gbs": round((LAYER_BYTES + O_BYTES) / (us_full_layer * 1e-6) / 1e9, 1),
         "lm_head_us": round(med_lm_ms * 1e3, 2),
         "lm_head_gbs": round(LMHEAD_BYTES / (med_lm_ms * 1e-3) / 1e9, 1),
         "eager_ms_per_step": round(eager_ms, 4),

@@ -19,6 +19,8 @@ independent uniform integer) and d, dmin drawn uniformly from [1e-4, 2e-3) and
 rounded to binary16 by numpy (round-to-nearest-even).
 
 Seeding: numpy PCG64 via ``default_rng([0x51344B, config, tensor_id, index])``.
+Configs: 0 tiny matvec, 1 QKV, 2 FFN, 3 lm_head, 4 prefill activations, 5 the
+attention output projection.
 Tensor ids: 0 = W / Wqkv / Wg, 1 = Wu, 2 = Wd, 3 = x / X. ``index`` is the layer
 or copy number. Draw order inside ``q4k_random``: the 144-byte rows of raw bytes
 first, then all d values, then all dmin values (row-major over blocks).
@@ -105,6 +107,12 @@ def lm_head(copy: int = 0, rows: int = VOCAB, cols: int = HIDDEN):
     """lm_head: W vocab x hidden; x ~ N(0,1) / sqrt(hidden)."""
     return {"W": q4k_random(rng_for(3, 0, copy), rows, cols),
             "x": normal_f32(rng_for(3, 3, copy), cols, scale=1.0 / np.sqrt(cols))}
+
+
+def o_proj(layer: int = 0, hidden: int = HIDDEN, q_dim: int = Q_ROWS):
+    """Attention output projection: W_o hidden x (8 heads x 256), input ~ N(0,1)."""
+    return {"W": q4k_random(rng_for(5, 0, layer), hidden, q_dim),
+            "x": normal_f32(rng_for(5, 3, layer), q_dim)}
 
 
 def prefill_x(seq: int = PREFILL_SEQ, hidden: int = HIDDEN, index: int = 0):

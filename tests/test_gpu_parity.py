@@ -153,6 +153,14 @@ def test_qkv_config(q4k, orc):
     assert_close(v.cpu().numpy(), ref[qr + kr:], A[qr + kr:], what="v")
 
 
+def test_o_projection_config(q4k, orc):
+    """Attention output projection at Gemma-3-4B shape: 2560 x 2048 (8 blocks per row)."""
+    c = inputs.o_proj()
+    y = gpu_matvec(q4k, c["W"], c["x"], inputs.HIDDEN, inputs.Q_ROWS)
+    ref, A = orc.matvec(c["W"], c["x"], inputs.HIDDEN, inputs.Q_ROWS)
+    assert_close(y, ref, A, what="o_proj 2560x2048")
+
+
 @pytest.mark.parametrize("qr,kr", [(8, 3), (1, 0), (0, 5), (37, 11)])
 def test_qkv_splits(q4k, orc, qr, kr):
     rng = np.random.default_rng(qr * 100 + kr)
