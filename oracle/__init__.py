@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.q4o_act_array.argtypes = [P, I64, ctypes.c_int, P]
         L.q4o_ffn.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P, P, P, P]
         L.q4o_topk.argtypes = [P, I64, ctypes.c_int, P, P]
+        L.q4o_logsumexp.argtypes = [P, I64]
+        L.q4o_logsumexp.restype = ctypes.c_double
+        L.q4o_softmax.argtypes = [P, I64, P]
         L.q4o_matmul.argtypes = [P, P, I64, I64, I64, P, P]
         L.q4o_ffn_prefill.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P, P]
         L.q4o_ffn_prefill_bf16.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P, P]
@@ -186,6 +189,20 @@ def topk(v, k: int):
     val = np.zeros(k, np.float64)
     lib().q4o_topk(_ptr(v), v.size, k, _ptr(idx), _ptr(val))
     return idx, val
+
+
+def logsumexp(v) -> float:
+    """log sum_i exp(v_i) in f64 (largest value taken out first); NaN if any v_i is NaN."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return float(lib().q4o_logsumexp(_ptr(v), v.size))
+
+
+def softmax(v) -> np.ndarray:
+    """p_i = exp(v_i - logsumexp(v)) in f64: the probabilities of the top-k predictions."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    p = np.zeros(v.size, np.float64)
+    lib().q4o_softmax(_ptr(v), v.size, _ptr(p))
+    return p
 
 
 def matmul(W, X, rows: int, cols: int):

@@ -28,6 +28,8 @@
  *  - GEGLU applies the activation to the gate: h = act(gate) * up;
  *  - GELU-tanh is 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)));
  *  - top-k order is value descending then index ascending, NaN ranks last;
+ *  - top-k probabilities are the plain softmax over all rows' logits (no
+ *    temperature or soft-capping), and a NaN logit makes them all NaN;
  *  - prefill is the decode definition applied per token, exactly (no bf16);
  *    q4o_ffn_prefill_bf16 additionally models bf16 operand rounding.
  */
@@ -263,6 +265,30 @@ void q4o_topk(const double *v, int64_t n, int k, int64_t *idx, double *val)
         val[i] = v[order[i]];
     }
     free(order);
+}
+
+/* ---- softmax over all rows (the probability of a top-k prediction) ----
+ * Source: infer-inference README, Overview example (the top prediction is
+ * shown with its probability in percent); Performance -- infer-inference,
+ * "Real vindex" table (top prediction with its probability).
+ * lse = log sum_i exp(v_i); p_i = exp(v_i - lse). The largest value m is
+ * taken out first, lse = m + log sum_i exp(v_i - m), an exact identity that
+ * keeps every exp() in (0, 1]. NaN anywhere makes lse (and so every p) NaN:
+ * NaN never wins the comparison for m, but exp(NaN - m) poisons the sum. */
+double q4o_logsumexp(const double *v, int64_t n)
+{
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i)
+        if (v[i] > m) m = v[i];
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += exp(v[i] - m);
+    return m + log(s);
+}
+
+void q4o_softmax(const double *v, int64_t n, double *p)
+{
+    const double lse = q4o_logsumexp(v, n);
+    for (int64_t i = 0; i < n; ++i) p[i] = exp(v[i] - lse);
 }
 
 /* ---- prefill: the decode definitions applied to each token row ---- */

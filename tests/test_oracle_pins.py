@@ -374,6 +374,80 @@ def test_topk_duplicated_rows_lower_index_first(orc):
     assert idx.tolist()[:3] == sorted({best, 37, 150})[:3]
 
 
+# ------------------------------------------------------------------ softmax ---
+
+def test_softmax_two_values_is_the_logistic_function(orc):
+    """Two classes: p_0 = 1 / (1 + e^(v1 - v0)), lse = v0 + log(1 + e^(v1 - v0))."""
+    for v0, v1 in [(0.0, 0.0), (1.5, -0.25), (-3.0, 2.0), (10.0, 10.5)]:
+        p = orc.softmax([v0, v1])
+        assert p[0] == pytest.approx(1.0 / (1.0 + math.exp(v1 - v0)), rel=1e-15)
+        assert p[1] == pytest.approx(1.0 / (1.0 + math.exp(v0 - v1)), rel=1e-15)
+        assert orc.logsumexp([v0, v1]) == pytest.approx(v0 + math.log1p(math.exp(v1 - v0)),
+                                                        rel=1e-15, abs=1e-15)
+
+
+def test_softmax_equal_values_are_uniform(orc):
+    for n in (1, 3, 262144):
+        v = np.full(n, -1.75)
+        p = orc.softmax(v)
+        assert np.allclose(p, 1.0 / n, rtol=1e-12, atol=0)
+        assert orc.logsumexp(v) == pytest.approx(-1.75 + math.log(n), rel=1e-14)
+
+
+def test_logsumexp_brute_force_on_small_inputs(orc):
+    """Without the max shift: log of the exactly rounded sum of exponentials."""
+    rng = np.random.default_rng(41)
+    for n in (1, 2, 5, 17, 100):
+        v = rng.uniform(-5, 5, n)
+        want = math.log(math.fsum(math.exp(t) for t in v))
+        assert orc.logsumexp(v) == pytest.approx(want, rel=1e-14, abs=1e-14)
+        p = orc.softmax(v)
+        assert np.allclose(p, [math.exp(t - want) for t in v], rtol=1e-13, atol=0)
+
+
+def test_softmax_sums_to_one_and_keeps_the_order(orc):
+    rng = np.random.default_rng(42)
+    v = rng.standard_normal(100000) * 4.0
+    p = orc.softmax(v)
+    assert math.fsum(p) == pytest.approx(1.0, abs=1e-12)
+    order = np.argsort(v, kind="stable")
+    assert np.all(np.diff(p[order]) >= 0)
+    assert np.all(p > 0)
+
+
+def test_softmax_shift_invariance_and_large_magnitudes(orc):
+    """softmax(v + c) = softmax(v) and lse(v + c) = lse(v) + c, also where
+    e^v alone overflows (v ~ 1000) or underflows (v ~ -1000)."""
+    v = np.array([0.0, 1.0, -1.0, 0.5])
+    p0 = orc.softmax(v)
+    lse0 = orc.logsumexp(v)
+    for c in (1000.0, -1000.0, 700.25):
+        p = orc.softmax(v + c)
+        assert np.all(np.isfinite(p))
+        assert np.allclose(p, p0, rtol=1e-12, atol=0)
+        assert orc.logsumexp(v + c) == pytest.approx(lse0 + c, rel=1e-14)
+    assert p0[1] == pytest.approx(math.e / (1 + math.e + 1 / math.e + math.exp(0.5)), rel=1e-15)
+
+
+def test_softmax_nan_poisons_everything(orc):
+    v = np.array([1.0, np.nan, 2.0])
+    assert math.isnan(orc.logsumexp(v))
+    assert np.all(np.isnan(orc.softmax(v)))
+
+
+def test_softmax_of_logits_is_shift_invariant_through_the_weights(orc):
+    """A row's dmin term m*dmin*sum(x) over a sub-block is a shift: with all
+    quants zero and the same dmin/min fields in every row, every logit is the
+    same number, so the probabilities are uniform."""
+    rows, cols = 7, 256
+    blk = pack_block(0.5, 0.25, [1] * 8, [3, 1, 4, 1, 5, 9, 2, 6], [0] * 256)
+    W = np.stack([blk] * rows)
+    x = np.random.default_rng(43).standard_normal(cols).astype(np.float32)
+    y, _ = orc.matvec(W, x, rows, cols)
+    assert np.all(y == y[0]) and y[0] != 0
+    assert np.allclose(orc.softmax(y), 1.0 / rows, rtol=1e-14, atol=0)
+
+
 # ---------------------------------------------------------------- prefill ---
 
 def test_matmul_rows_equal_matvec(orc):
