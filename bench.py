@@ -3,7 +3,7 @@
 A step is one decoded token's Q4_K work at Gemma-3-4B shapes: for each of 34
 independently seeded layers the fused QKV projection (4096 x 2560) and the
 gated FFN (gate+up 2 x 10240 x 2560 -> GELU-tanh -> down 2560 x 10240), then the
-lm_head (262144 x 2560) with top-5. All weights (2.1 GB) are resident in HBM
+lm_head (262144 x 2560) with top-5 and their softmax probabilities. All weights (2.1 GB) are resident in HBM
 before timing; 34 distinct layers exceed the 256 MB Infinity Cache, so each
 step streams its weights from HBM. Steps are replayed from HIP graphs captured
 once (launch-bound inner loop); the eager launch rate is reported beside it.
@@ -49,7 +49,7 @@ DOWN_BYTES = wbytes(HIDDEN, INTER) + INTER * 4 + HIDDEN * 4
 LAYER_BYTES = QKV_BYTES + GATE_UP_BYTES + DOWN_BYTES
 # The attention output projection (2560 x 2048), timed in the full-layer sequence
 O_BYTES = wbytes(HIDDEN, QROWS) + QROWS * 4 + HIDDEN * 4
-LMHEAD_BYTES = wbytes(VOCAB, HIDDEN) + HIDDEN * 4 + VOCAB * 4 + TOPK * 8
+LMHEAD_BYTES = wbytes(VOCAB, HIDDEN) + HIDDEN * 4 + VOCAB * 4 + TOPK * 12 + 4
 STEP_BYTES = LAYERS * LAYER_BYTES + LMHEAD_BYTES
 # Prefill FFN, 64 tokens: weights once, X in, Y out; 2 flops per weight per token.
 PREFILL_SEQ = 64
@@ -102,7 +102,9 @@ def cpu_baseline(data, budget_s: float):
             break
     lm_rows = 16384
     lm = data["lm_host"]
-    oracle.matvec(lm["W"][:lm_rows], lm["x"], lm_rows, HIDDEN)
+    y_lm, _ = oracle.matvec(lm["W"][:lm_rows], lm["x"], lm_rows, HIDDEN)
+    oracle.topk(y_lm, TOPK)
+    oracle.softmax(y_lm)
     done_bytes += wbytes(lm_rows, HIDDEN) + HIDDEN * 4 + lm_rows * 4
     dt = time.perf_counter() - t0
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -180,6 +182,8 @@ def main() -> int:
     logits = torch.empty(VOCAB, device=dev)
     top_idx = torch.empty(TOPK, dtype=torch.int32, device=dev)
     top_val = torch.empty(TOPK, device=dev)
+    top_prob = torch.empty(TOPK, device=dev)
+    lse = torch.empty(1, device=dev)
     lm_ws = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(VOCAB, HIDDEN, TOPK))
     GELU = q4k.Q4K_ACT_GELU_TANH
     do_prefill = not args.no_prefill and args.kernel_only in ("", "prefill")
@@ -209,8 +213,8 @@ def main() -> int:
             q4k.q4k_ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], y, HIDDEN, INTER, GELU, h)
 
     def run_lmhead():
-        q4k.q4k_lmhead_topk(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx, top_val,
-                            lm_ws)
+        q4k.q4k_lmhead_topk_probs(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx,
+                                  top_val, top_prob, lse, lm_ws)
 
     if args.kernel_only == "copy":
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -337,6 +341,33 @@ def main() -> int:
     us_full_layer = full_ms[len(full_ms) // 2] * 1e3 / LAYERS
     log(f"full layer (QKV + O + FFN): {us_full_layer:.2f} us")
 
+    # ------------- lm_head: cost of the softmax probabilities beside top-k
+    def time_graph(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            g.replay()
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a_ev.elapsed_time(b_ev) * 1e3 / n)
+        return sorted(ts)[1]
+
+    def run_lmhead_plain():
+        q4k.q4k_lmhead_topk(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx, top_val,
+                            lm_ws)
+
+    lm_probs_us = time_graph(run_lmhead, 10)
+    lm_plain_us = time_graph(run_lmhead_plain, 10)
+    log(f"lm_head top-5: {lm_plain_us:.2f} us; with probabilities: {lm_probs_us:.2f} us")
+
     # ------------------------------------------ prefill FFN (matrix cores)
     prefill = None
     if do_prefill:
@@ -400,7 +431,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "gemma3-4b decode step: 34 x (fused QKV 4096x2560 + gated FFN "
-                        "10240x2560 gate/up, 2560x10240 down, GELU-tanh) + lm_head 262144x2560 top-5, "
+                        "10240x2560 gate/up, 2560x10240 down, GELU-tanh) + lm_head 262144x2560 top-5 with softmax probabilities, "
                         "Q4_K weights, f32 activations",
             "layers": LAYERS, "hidden": HIDDEN, "inter": INTER, "vocab": VOCAB, "top_k": TOPK,
             "graph_replay": use_graph,
@@ -413,6 +444,8 @@ def main() -> int:
         "full_layer_gbs": round((LAYER_BYTES + O_BYTES) / (us_full_layer * 1e-6) / 1e9, 1),
         "lm_head_us": round(med_lm_ms * 1e3, 2),
         "lm_head_gbs": round(LMHEAD_BYTES / (med_lm_ms * 1e-3) / 1e9, 1),
+        "lm_head_topk_only_us": round(lm_plain_us, 2),
+        "lm_head_with_probs_us": round(lm_probs_us, 2),
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {
             "kernel": "q4k gate_up (fused gate+up + GELU-tanh), 2 x 10240x2560",

@@ -112,7 +112,8 @@ size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter);
 int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
             int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace of q4k_lmhead_topk: per-workgroup top-k candidates. */
+/* Workspace of q4k_lmhead_topk and q4k_lmhead_topk_probs: per-workgroup
+ * top-k candidates and softmax partials. */
 size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k);
 
 /* logits = W x over all rows (the vocabulary), then the k largest logits in
@@ -125,6 +126,19 @@ size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k);
 int q4k_lmhead_topk(const void *W, const float *x, float *logits, int64_t rows, int64_t cols,
                     int k, int32_t *top_idx, float *top_val, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* q4k_lmhead_topk, plus the softmax over all rows' logits:
+ * lse[0] = log sum_i exp(logits[i]) and top_prob[r] = exp(top_val[r] - lse),
+ * the probability of the r-th prediction (f32[k]). Computed in f32 in the same
+ * pass: each workgroup reduces (max, sum of exp(l - max)) over its rows and
+ * the merge combines them. A NaN logit makes lse and every top_prob NaN.
+ * top_prob and lse must not overlap each other or any other argument.
+ * Source: infer-inference README, Overview example (top prediction printed
+ * with its probability); Performance -- infer-inference, "Real vindex" table
+ * (top prediction with its probability). */
+int q4k_lmhead_topk_probs(const void *W, const float *x, float *logits, int64_t rows,
+                          int64_t cols, int k, int32_t *top_idx, float *top_val, float *top_prob,
+                          float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace of q4k_matmul (bf16 copy of X for seq >= 64; 0 otherwise). */
 size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq);

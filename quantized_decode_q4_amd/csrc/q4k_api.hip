@@ -146,37 +146,73 @@ Q4K_EXPORT int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const flo
                                       (float *)ws, as_stream(stream)));
 }
 
+// lm_head workspace: the per-workgroup candidate lists (k keys of 8 bytes
+// each), then the per-workgroup softmax partials (float2).
+static size_t lmhead_cand_bytes(int64_t rows, int64_t cols, int k)
+{
+    return round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * (size_t)k * 8, 256);
+}
+
 Q4K_EXPORT size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k)
 {
     if (!rows_ok(rows) || !cols_ok(cols) || rows == 0 || k < 1 || k > Q4K_TOPK_MAX) return 0;
-    return round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * (size_t)k * 8, 256);
+    return lmhead_cand_bytes(rows, cols, k) +
+           round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * 8, 256);
+}
+
+// Shared by q4k_lmhead_topk (probs == false: top_prob and lse unused) and
+// q4k_lmhead_topk_probs.
+static int lmhead_call(const void *W, const float *x, float *logits, int64_t rows, int64_t cols,
+                       int k, int32_t *top_idx, float *top_val, float *top_prob, float *lse,
+                       bool probs, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
+    if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
+    if (q4k::lmhead_max_wgs(rows, cols) > q4k::kMergeListsMax) return Q4K_ERR_SHAPE;
+    if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
+    if (probs && (!top_prob || !lse)) return Q4K_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||
+        !aligned(top_val, 4))
+        return Q4K_ERR_ALIGN;
+    if (probs && (!aligned(top_prob, 4) || !aligned(lse, 4))) return Q4K_ERR_ALIGN;
+    const size_t need = q4k_lmhead_workspace_bytes(rows, cols, k);
+    if (!ws || ws_bytes < need) return Q4K_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return Q4K_ERR_ALIGN;
+    const Span in[2] = {span(W, wbytes(rows, cols)), span(x, cols * 4)};
+    const int nout = probs ? 6 : 4;
+    const Span out[6] = {span(logits, rows * 4),       span(top_idx, (int64_t)k * 4),
+                         span(top_val, (int64_t)k * 4), span(ws, (int64_t)need),
+                         span(top_prob, probs ? (int64_t)k * 4 : 0),
+                         span(lse, probs ? 4 : 0)};
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlap(out[i], in[j])) return Q4K_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return Q4K_ERR_ALIAS;
+    }
+    uint8_t *w8 = (uint8_t *)ws;
+    float2 *stats = probs ? (float2 *)(w8 + lmhead_cand_bytes(rows, cols, k)) : nullptr;
+    return hip_status(q4k::launch_lmhead_topk((const uint8_t *)W, x, logits, rows, cols, k,
+                                              (uint64_t *)ws, top_idx, top_val, stats,
+                                              probs ? top_prob : nullptr, probs ? lse : nullptr,
+                                              as_stream(stream)));
 }
 
 Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int64_t rows,
                                int64_t cols, int k, int32_t *top_idx, float *top_val, void *ws,
                                size_t ws_bytes, void *stream)
 {
-    if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
-    if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
-    if (q4k::lmhead_max_wgs(rows, cols) > q4k::kMergeListsMax) return Q4K_ERR_SHAPE;
-    if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
-    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||
-        !aligned(top_val, 4))
-        return Q4K_ERR_ALIGN;
-    const size_t need = q4k_lmhead_workspace_bytes(rows, cols, k);
-    if (!ws || ws_bytes < need) return Q4K_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return Q4K_ERR_ALIGN;
-    const Span in[2] = {span(W, wbytes(rows, cols)), span(x, cols * 4)};
-    const Span out[4] = {span(logits, rows * 4), span(top_idx, (int64_t)k * 4),
-                         span(top_val, (int64_t)k * 4), span(ws, (int64_t)need)};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 2; ++j)
-            if (overlap(out[i], in[j])) return Q4K_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(out[i], out[j])) return Q4K_ERR_ALIAS;
-    }
-    return hip_status(q4k::launch_lmhead_topk((const uint8_t *)W, x, logits, rows, cols, k,
-                                              (uint64_t *)ws, top_idx, top_val, as_stream(stream)));
+    return lmhead_call(W, x, logits, rows, cols, k, top_idx, top_val, nullptr, nullptr, false, ws,
+                       ws_bytes, stream);
+}
+
+Q4K_EXPORT int q4k_lmhead_topk_probs(const void *W, const float *x, float *logits, int64_t rows,
+                                     int64_t cols, int k, int32_t *top_idx, float *top_val,
+                                     float *top_prob, float *lse, void *ws, size_t ws_bytes,
+                                     void *stream)
+{
+    return lmhead_call(W, x, logits, rows, cols, k, top_idx, top_val, top_prob, lse, true, ws,
+                       ws_bytes, stream);
 }
 
 Q4K_EXPORT size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq)

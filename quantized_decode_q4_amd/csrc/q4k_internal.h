@@ -34,9 +34,12 @@ hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, c
 // any device uses for the shape (sizes the workspace).
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols);
 int64_t lmhead_max_wgs(int64_t rows, int64_t cols);
+// With stats (lmhead_max_wgs float2 partials), also the softmax over all
+// rows: lse[0] and top_prob[k]; stats == nullptr skips both.
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,
                               int64_t cols, int k, uint64_t *cand, int32_t *top_idx,
-                              float *top_val, hipStream_t s);
+                              float *top_val, float2 *stats, float *top_prob, float *lse,
+                              hipStream_t s);
 
 // Matrix-core prefill (q4k_mm.hip), for seq >= 64 tokens. Workspace sizes
 // (bytes) for the current device, and the launches that carve them.

@@ -98,6 +98,7 @@ struct RowsArgs {
     float *o1;
     float *o2;
     uint64_t *cand;          // EPI_LOGITS
+    float2 *stats;           // EPI_LOGITS, optional: per-workgroup (max, sum of exp(l - max))
     int64_t rows;
     int64_t split0;
     int64_t split1;
@@ -372,28 +373,84 @@ __device__ __forceinline__ uint64_t topk_key(float v, uint32_t idx)
     return ((uint64_t)hi << 32) | (uint64_t)(~idx);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off)
+// The logit a key was made from (the NaN class decodes to a NaN; -0 was
+// folded into +0).
+__device__ __forceinline__ float topk_key_value(uint64_t key)
 {
-    const uint32_t lo = __shfl_xor((unsigned int)(v & 0xFFFFFFFFu), off);
-    const uint32_t hi = __shfl_xor((unsigned int)(v >> 32), off);
+    const uint32_t hi = (uint32_t)(key >> 32);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint64_t join_u64(uint32_t hi, uint32_t lo)
+{
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Workgroup-wide maximum of a 64-bit key (all threads get the result).
+// Largest 64-bit key over the 64 lanes of a wave (every lane gets it), in
+// the same pattern as wave_sum_mod: rotations by 1, 2, 4, 8 inside 16-lane
+// rows, then the row and half swaps (inline asm, see wave_sum_mod).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#define Q4K_ROR_MAX(C)                                                                     \
+    {                                                                                      \
+        const uint64_t o = join_u64(dpp_u32<C>((uint32_t)(v >> 32)), dpp_u32<C>((uint32_t)v)); \
+        v = o > v ? o : v;                                                                 \
+    }
+    Q4K_ROR_MAX(0x121)
+    Q4K_ROR_MAX(0x122)
+    Q4K_ROR_MAX(0x124)
+    Q4K_ROR_MAX(0x128)
+#undef Q4K_ROR_MAX
+    {
+        uint32_t xl = (uint32_t)v, yl = xl, xh = (uint32_t)(v >> 32), yh = xh;
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(xl), "+v"(yl));
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(xh), "+v"(yh));
+        const uint64_t a = join_u64(xh, xl), b = join_u64(yh, yl);
+        v = a > b ? a : b;
+    }
+    {
+        uint32_t xl = (uint32_t)v, yl = xl, xh = (uint32_t)(v >> 32), yh = xh;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(xl), "+v"(yl));
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(xh), "+v"(yh));
+        const uint64_t a = join_u64(xh, xl), b = join_u64(yh, yl);
+        v = a > b ? a : b;
+    }
+    return v;
+}
+
+// Workgroup-wide maximum of a key with one barrier: wave maxima go to
+// scratch[wave], which the caller alternates between two buffers from one
+// call to the next (a buffer is rewritten only after the next call's
+// barrier, when every thread has read it).
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
 {
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t o = shfl_xor_u64(v, off);
-        v = o > v ? o : v;
-    }
+    v = wave_max_u64(v);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = (blockDim.x + 63) >> 6;
     if (lane == 0) scratch[wave] = v;
     __syncthreads();
-    uint64_t m = 0;
-    for (int w = 0; w < nwaves; ++w) m = scratch[w] > m ? scratch[w] : m;
-    __syncthreads();
+    uint64_t m = scratch[0];
+    for (int w = 1; w < nwaves; ++w) m = scratch[w] > m ? scratch[w] : m;
     return m;
+}
+
+// Workgroup-wide sum with one barrier (fixed order: deterministic).
+__device__ __forceinline__ float block_sum_f32(float v, float *scratch)
+{
+    v = wave_sum_mod<1>(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = (blockDim.x + 63) >> 6;
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    float r = scratch[0];
+    for (int w = 1; w < nwaves; ++w) r += scratch[w];
+    return r;
 }
 
 // ----------------------------------------------------------- the kernel ---
@@ -419,7 +476,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     __shared__ float red[2][NW][FB * NMAT * RPS];
     __shared__ float lg[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint8_t taken[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
-    __shared__ uint64_t keys_scratch[EPI == EPI_LOGITS ? NW : 1];
+    __shared__ uint64_t keys_scratch[2][EPI == EPI_LOGITS ? NW : 1];
+    __shared__ float sum_scratch[EPI == EPI_LOGITS ? NW : 1];
     extern __shared__ uint4 xlds_v[];   // XS_LDS: planes of x (planes_bytes(cols))
     uint8_t *const xlds = reinterpret_cast<uint8_t *>(xlds_v);
 
@@ -639,10 +697,13 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 
     if (EPI == EPI_LOGITS) {
         // Per-workgroup top-k of its rows, written in rank order: k rounds of
-        // a workgroup-wide max over orderable keys; the winner is removed.
+        // a workgroup-wide max over orderable keys. The thread that owns the
+        // winning row (row j is scanned by thread j mod blockDim) marks it
+        // taken, so the mark needs no barrier of its own.
         __syncthreads();
         const int n = (int)(row_stop - row_begin);
         uint64_t *out = a.cand + (int64_t)blockIdx.x * a.k;
+        float wg_max = 0.f;
         for (int round = 0; round < a.k; ++round) {
             uint64_t best = 0;
             for (int j = t; j < n; j += blockDim.x) {
@@ -650,12 +711,24 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 const uint64_t kk = topk_key(lg[j], (uint32_t)(row_begin + j));
                 best = kk > best ? kk : best;
             }
-            const uint64_t win = block_max_u64(best, keys_scratch);
-            if (t == 0) {
-                out[round] = win;
-                if (win != 0) taken[(int64_t)(~(uint32_t)(win & 0xFFFFFFFFu)) - row_begin] = 1;
+            const uint64_t win = block_max_u64(best, keys_scratch[round & 1]);
+            if (round == 0) wg_max = topk_key_value(win);
+            if (win != 0) {
+                const int j = (int)((int64_t)(~(uint32_t)(win & 0xFFFFFFFFu)) - row_begin);
+                if (j % (int)blockDim.x == t) taken[j] = 1;
             }
-            __syncthreads();
+            if (t == 0) out[round] = win;
+        }
+        if (a.stats) {
+            // softmax partial of this workgroup: m = its largest logit (the
+            // first winner), s = sum of exp(l - m). When m is -inf (every row
+            // -inf or NaN) the exponent is taken against 0 instead, so that -inf
+            // rows add 0 and NaN rows poison the sum.
+            const float base = wg_max == -INFINITY ? 0.f : wg_max;
+            float sum = 0.f;
+            for (int j = t; j < n; j += blockDim.x) sum += expf(lg[j] - base);
+            sum = block_sum_f32(sum, sum_scratch);
+            if (t == 0) a.stats[blockIdx.x] = make_float2(wg_max, sum);
         }
     }
 }
@@ -663,50 +736,112 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 // Merge of the per-workgroup candidate lists (each sorted in rank order) into
 // the global top-k: a k-way merge. Thread t owns lists t, t+256, ...; each
 // round the workgroup takes the largest list head and that list advances.
+// When all lists fit, they are first copied to LDS (all loads issued at
+// once), so that advancing a list costs an LDS read instead of a dependent
+// global load.
+// With stats, the per-workgroup softmax partials (m_w, s_w) are combined
+// against M, the largest logit (the first winner): S = sum_w s_w exp(m_w - M),
+// lse = M + log S, and a winner's probability is exp(l - M) / S.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeListsPerThread = 4;   // up to 1024 lists
+constexpr int kMergeStagedPerThread = 24; // 48 KB of staged candidates
+constexpr int kMergeLdsKeys = kMergeStagedPerThread * kMergeThreads;
 
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_t *cand, int nlists,
                                                                     int k, const float *logits,
                                                                     int32_t *top_idx,
-                                                                    float *top_val)
+                                                                    float *top_val,
+                                                                    const float2 *stats,
+                                                                    float *top_prob, float *lse)
 {
-    __shared__ uint64_t scratch[kMergeThreads / 64];
+    __shared__ uint64_t key_scratch[2][kMergeThreads / 64];
+    __shared__ float sum_scratch[kMergeThreads / 64];
+    __shared__ uint64_t staged[kMergeLdsKeys];
+    __shared__ uint64_t wins[kTopkMax];
     const int t = threadIdx.x;
+    const int total = nlists * k;
+    const bool in_lds = total <= kMergeLdsKeys;
+    // the partials and the staged lists are loaded together: one memory latency
+    float2 st[kMergeListsPerThread];
+#pragma unroll
+    for (int i = 0; i < kMergeListsPerThread; ++i) {
+        const int l = t + i * kMergeThreads;
+        st[i] = (stats && l < nlists) ? stats[l] : make_float2(-INFINITY, 0.f);
+    }
+    if (in_lds) {
+        uint64_t v[kMergeStagedPerThread];
+#pragma unroll
+        for (int i = 0; i < kMergeStagedPerThread; ++i) {
+            const int j = t + i * kMergeThreads;
+            v[i] = j < total ? cand[j] : 0ull;
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeStagedPerThread; ++i) {
+            const int j = t + i * kMergeThreads;
+            if (j < total) staged[j] = v[i];
+        }
+    }
+    __syncthreads();
+    auto key_at = [&](int l, int pos) -> uint64_t {
+        const int i = l * k + pos;
+        return in_lds ? staged[i] : cand[i];
+    };
     int pos[kMergeListsPerThread];
     uint64_t head[kMergeListsPerThread];
 #pragma unroll
     for (int i = 0; i < kMergeListsPerThread; ++i) {
         const int l = t + i * kMergeThreads;
         pos[i] = 0;
-        head[i] = l < nlists ? cand[(int64_t)l * k] : 0ull;
+        head[i] = l < nlists ? key_at(l, 0) : 0ull;
     }
+    float M = 0.f;
     for (int round = 0; round < k; ++round) {
         uint64_t best = 0;
 #pragma unroll
         for (int i = 0; i < kMergeListsPerThread; ++i) best = head[i] > best ? head[i] : best;
-        const uint64_t win = block_max_u64(best, scratch);
+        const uint64_t win = block_max_u64(best, key_scratch[round & 1]);
+        if (round == 0) M = topk_key_value(win);
         if (win != 0) {
 #pragma unroll
             for (int i = 0; i < kMergeListsPerThread; ++i) {
                 if (head[i] == win) {  // keys are unique (they embed the row)
                     const int l = t + i * kMergeThreads;
                     ++pos[i];
-                    head[i] = pos[i] < k ? cand[(int64_t)l * k + pos[i]] : 0ull;
+                    head[i] = pos[i] < k ? key_at(l, pos[i]) : 0ull;
                 }
             }
         }
-        if (t == 0) {
-            if (win == 0) {
-                top_idx[round] = -1;
-                top_val[round] = __uint_as_float(0x7FC00000u);
-            } else {
-                const uint32_t idx = ~(uint32_t)(win & 0xFFFFFFFFu);
-                top_idx[round] = (int32_t)idx;
-                top_val[round] = logits[idx];
-            }
+        if (t == 0) wins[round] = win;
+    }
+    const float base = M == -INFINITY ? 0.f : M;
+    float S = 0.f;
+    if (stats) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMergeListsPerThread; ++i)
+            if (st[i].y != 0.f) sum += st[i].y * expf(st[i].x - base);  // NaN partials propagate
+        S = block_sum_f32(sum, sum_scratch);   // its barrier also publishes wins[]
+    } else {
+        __syncthreads();
+    }
+    if (t < k) {
+        const uint64_t win = wins[t];
+        if (win == 0) {
+            top_idx[t] = -1;
+            top_val[t] = __uint_as_float(0x7FC00000u);
+            if (stats) top_prob[t] = __uint_as_float(0x7FC00000u);
+        } else {
+            const uint32_t idx = ~(uint32_t)(win & 0xFFFFFFFFu);
+            // the key holds the logit's bits, except the sign of a zero and a
+            // NaN's payload: only those are read back from the logits
+            float l = topk_key_value(win);
+            if (!(fabsf(l) > 0.f)) l = logits[idx];
+            top_idx[t] = (int32_t)idx;
+            top_val[t] = l;
+            if (stats) top_prob[t] = expf(l - base) / S;
         }
     }
+    if (stats && t == 0) *lse = base + logf(S);
 }
 
 // ---------------------------------------------------------------- host ---
@@ -890,20 +1025,22 @@ int64_t lmhead_max_wgs(int64_t rows, int64_t cols)
 
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,
                               int64_t cols, int k, uint64_t *cand, int32_t *top_idx,
-                              float *top_val, hipStream_t s)
+                              float *top_val, float2 *stats, float *top_prob, float *lse,
+                              hipStream_t s)
 {
     RowsArgs a = base_args(rows, cols);
     a.W0 = W;
     a.x = x;
     a.o0 = logits;
     a.cand = cand;
+    a.stats = stats;
     a.k = k;
     const Shape sh = pick_shape(cols);
     const int64_t nwg = lmhead_num_wgs(rows, cols);
     hipError_t e = launch_rows_bfp<1, EPI_LOGITS, Q4K_LMHEAD_D>(a, sh.rps, sh.threads, nwg, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeThreads), 0, s, cand, (int)nwg, k,
-                       logits, top_idx, top_val);
+                       logits, top_idx, top_val, stats, top_prob, lse);
     return hipGetLastError();
 }
 

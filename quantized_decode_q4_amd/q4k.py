@@ -53,6 +53,7 @@ _SIGS = {
     "q4k_ffn": ([_P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P], _INT),
     "q4k_lmhead_workspace_bytes": ([_I64, _I64, _INT], _SZ),
     "q4k_lmhead_topk": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _SZ, _P], _INT),
+    "q4k_lmhead_topk_probs": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P, _P, _SZ, _P], _INT),
     "q4k_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4k_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "q4k_ffn_prefill_workspace_bytes": ([_I64, _I64, _I64], _SZ),
@@ -139,6 +140,15 @@ def q4k_lmhead_topk(W, x, logits, rows: int, cols: int, k: int, top_idx, top_val
     _check(lib.q4k_lmhead_topk(_ptr(W), _ptr(x), _ptr(logits), rows, cols, k, _ptr(top_idx),
                                _ptr(top_val), _ptr(ws), ws_bytes, _stream(stream)),
            "q4k_lmhead_topk")
+
+
+def q4k_lmhead_topk_probs(W, x, logits, rows: int, cols: int, k: int, top_idx, top_val, top_prob,
+                          lse, ws, ws_bytes: int | None = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = _nbytes(ws)
+    _check(lib.q4k_lmhead_topk_probs(_ptr(W), _ptr(x), _ptr(logits), rows, cols, k, _ptr(top_idx),
+                                     _ptr(top_val), _ptr(top_prob), _ptr(lse), _ptr(ws), ws_bytes,
+                                     _stream(stream)), "q4k_lmhead_topk_probs")
 
 
 def q4k_matmul_workspace_bytes(rows: int, cols: int, seq: int) -> int:

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["q4k_matvec", "q4k_qkv", "q4k_ffn", "q4k_gate_up", "q4k_lmhead_topk", "q4k_matmul",
+    for n in ["q4k_matvec", "q4k_qkv", "q4k_ffn", "q4k_gate_up", "q4k_lmhead_topk",
+              "q4k_lmhead_topk_probs", "q4k_matmul",
               "q4k_ffn_prefill", "q4k_status_string", "q4k_last_hip_error",
               "q4k_ffn_workspace_bytes", "q4k_lmhead_workspace_bytes",
               "q4k_matmul_workspace_bytes", "q4k_ffn_prefill_workspace_bytes"]:
@@ -118,6 +119,25 @@ def test_lmhead_validation():
     assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, E, C + 64, need, S) == q4k.Q4K_ERR_ALIAS
     # a vocabulary too large for the single-workgroup merge at k = 64
     assert L.q4k_lmhead_topk(A, B, C, 5_000_000, 256, 64, D, E, F, 1 << 40, S) == q4k.Q4K_ERR_SHAPE
+
+
+def test_lmhead_probs_validation():
+    G = 0x7F6000000000
+    H = 0x7F7000000000
+    P = L.q4k_lmhead_topk_probs
+    need = q4k.q4k_lmhead_workspace_bytes(1000, 256, 5)
+    assert P(A, B, C, 1000, 256, 0, D, E, G, H, F, need, S) == q4k.Q4K_ERR_K
+    assert P(A, B, C, 1000, 256, 5, D, E, None, H, F, need, S) == q4k.Q4K_ERR_NULL
+    assert P(A, B, C, 1000, 256, 5, D, E, G, None, F, need, S) == q4k.Q4K_ERR_NULL
+    assert P(A, B, C, 1000, 256, 5, D, E, G + 2, H, F, need, S) == q4k.Q4K_ERR_ALIGN
+    assert P(A, B, C, 1000, 256, 5, D, E, G, H + 1, F, need, S) == q4k.Q4K_ERR_ALIGN
+    assert P(A, B, C, 1000, 256, 5, D, E, G, H, F, need - 8, S) == q4k.Q4K_ERR_WORKSPACE
+    assert P(A, B, C, 1000, 256, 5, D, E, G, G + 16, F, need, S) == q4k.Q4K_ERR_ALIAS  # lse in probs
+    assert P(A, B, C, 1000, 256, 5, D, E, E, H, F, need, S) == q4k.Q4K_ERR_ALIAS      # probs on vals
+    assert P(A, B, C, 1000, 256, 5, D, E, G, F + 64, F, need, S) == q4k.Q4K_ERR_ALIAS  # lse in ws
+    assert P(A, B, C, 1000, 256, 5, D, E, G, A + 4, F, need, S) == q4k.Q4K_ERR_ALIAS   # lse on W
+    assert P(A, B, C, 1000, 256, 5, D, E, B, H, F, need, S) == q4k.Q4K_ERR_ALIAS       # probs on x
+    assert P(A, B, C, 5_000_000, 256, 64, D, E, G, H, F, 1 << 40, S) == q4k.Q4K_ERR_SHAPE
 
 
 def test_prefill_validation():

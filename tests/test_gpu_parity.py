@@ -4,6 +4,8 @@ Pass rule for the f32 paths, per output element: |gpu - oracle| <= 1e-4 * A,
 A = sum_j |w_ij x_j| from the oracle. Top-k indices must match exactly except
 where two candidates are indistinguishable at that tolerance.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -324,6 +326,121 @@ def test_lmhead_nan_rows_rank_last(q4k, orc):
     ref, _ = orc.matvec(W[:12], x, 12, cols)
     ridx, _ = orc.topk(ref, 12)
     assert ti.tolist() == ridx.tolist()
+
+
+# ------------------------------------------------- lm_head probabilities ---
+
+def gpu_lmhead_probs(q4k, W, x, rows, cols, k):
+    logits = torch.empty(rows, device="cuda")
+    ti = torch.empty(k, dtype=torch.int32, device="cuda")
+    tv = torch.empty(k, device="cuda")
+    tp = torch.full((k,), float("nan"), device="cuda")
+    lse = torch.full((1,), float("nan"), device="cuda")
+    ws = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(rows, cols, k))
+    q4k.q4k_lmhead_topk_probs(dev(W), dev(x), logits, rows, cols, k, ti, tv, tp, lse, ws)
+    torch.cuda.synchronize()
+    return (logits.cpu().numpy(), ti.cpu().numpy(), tv.cpu().numpy(), tp.cpu().numpy(),
+            float(lse.cpu().numpy()[0]))
+
+
+def check_probs(logits, ti, tv, tp, lse, ref, A, what):
+    """Against the f64 softmax of the exact logits. A logit error of at most
+    TOL*A_j moves lse by at most TOL * sum_j p_j A_j and log p_i by that plus
+    TOL*A_i; the f32 exp/log/sum roundings add well under 1e-5."""
+    orc = orcmod()
+    p_ref = orc.softmax(ref)
+    lse_ref = orc.logsumexp(ref)
+    pA = float(np.dot(p_ref, A))
+    err_lse = abs(lse - lse_ref)
+    bound_lse = TOL * pA + 1e-5 + 1e-6 * abs(lse_ref)
+    print(f"{what}: lse {lse:.7g} (oracle {lse_ref:.7g}), |err| {err_lse:.3e} <= {bound_lse:.3e}",
+          flush=True)
+    assert err_lse <= bound_lse
+    worst = 0.0
+    for r in range(len(ti)):
+        i = int(ti[r])
+        assert tp[r] > 0, (r, tp[r])
+        e = abs(math.log(float(tp[r])) - math.log(p_ref[i]))
+        b = TOL * (A[i] + pA) + 2e-5
+        worst = max(worst, e / b)
+        assert e <= b, (what, r, i, float(tp[r]), p_ref[i], e, b)
+    print(f"{what}: top-{len(ti)} log-prob |err| / bound <= {worst:.3f}; "
+          f"p = {[float(v) for v in tp[:5]]}", flush=True)
+    # the GPU's own numbers agree: top_prob = exp(top_val - lse), and its
+    # logits' probabilities sum to one
+    assert np.allclose(tp, np.exp(tv.astype(np.float64) - lse), rtol=1e-5, atol=0)
+    total = math.fsum(np.exp(logits.astype(np.float64) - lse))
+    assert abs(total - 1.0) <= 1e-5 + 1e-6 * abs(lse), total
+
+
+def test_lmhead_probs_config_top5(q4k, orc):
+    c = inputs.lm_head()
+    rows, cols = inputs.VOCAB, inputs.HIDDEN
+    logits, ti, tv, tp, lse = gpu_lmhead_probs(q4k, c["W"], c["x"], rows, cols, 5)
+    ref, A = orc.matvec(c["W"], c["x"], rows, cols)
+    assert_close(logits, ref, A, what="lm_head logits (probs entry)")
+    topk_ok(ti, tv, ref, A, 5)
+    check_probs(logits, ti, tv, tp, lse, ref, A, "lm_head 262144x2560 top-5")
+    # the plain entry point gives the same logits and top-k, bit for bit
+    l2, ti2, tv2 = gpu_lmhead(q4k, c["W"], c["x"], rows, cols, 5)
+    assert np.array_equal(l2.view(np.uint32), logits.view(np.uint32))
+    assert np.array_equal(ti2, ti) and np.array_equal(tv2.view(np.uint32), tv.view(np.uint32))
+
+
+# (rows, cols, k, x scale): one row (p = 1), peaked distributions (x scaled up:
+# logits past the f32 range of exp, so the largest value must be taken out
+# first), the k bound, ragged rows, many workgroups with few rows each.
+@pytest.mark.parametrize("rows,cols,k,scale", [(1, 256, 1, 1.0), (100, 256, 7, 3.0),
+                                               (2000, 256, 5, 8.0), (4097, 512, 64, 1.0),
+                                               (30000, 1024, 5, 0.2), (100000, 256, 5, 0.0625),
+                                               (3000, 20480, 9, 0.05)])
+def test_lmhead_probs_shapes(q4k, orc, rows, cols, k, scale):
+    rng = np.random.default_rng(rows + 3 * cols + k)
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols, scale=scale)
+    logits, ti, tv, tp, lse = gpu_lmhead_probs(q4k, W, x, rows, cols, k)
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(logits, ref, A, what=f"lm_head {rows}x{cols}")
+    topk_ok(ti, tv, ref, A, k)
+    check_probs(logits, ti, tv, tp, lse, ref, A, f"probs {rows}x{cols} k={k} scale={scale}")
+    if rows == 1:
+        assert tp[0] == 1.0 and lse == logits[0]
+
+
+def test_lmhead_probs_equal_rows_are_uniform(q4k, orc):
+    rng = np.random.default_rng(33)
+    rows, cols, k = 5000, 512, 8
+    W = np.repeat(inputs.q4k_random(rng, 1, cols), rows, axis=0)
+    x = inputs.normal_f32(rng, cols)
+    logits, ti, tv, tp, lse = gpu_lmhead_probs(q4k, W, x, rows, cols, k)
+    assert ti.tolist() == list(range(k))
+    assert np.allclose(tp, 1.0 / rows, rtol=1e-5, atol=0)
+    assert abs(lse - (float(logits[0]) + math.log(rows))) <= 1e-5 * (1 + abs(lse))
+
+
+def test_lmhead_probs_nan_row(q4k, orc):
+    rng = np.random.default_rng(34)
+    rows, cols, k = 3000, 256, 5
+    W = inputs.q4k_random(rng, rows, cols)
+    W[1234, 0:2] = np.array([0x00, 0x7E], np.uint8)   # d = binary16 NaN
+    x = inputs.normal_f32(rng, cols)
+    logits, ti, tv, tp, lse = gpu_lmhead_probs(q4k, W, x, rows, cols, k)
+    assert math.isnan(lse) and np.all(np.isnan(tp))
+    _, ti2, _ = gpu_lmhead(q4k, W, x, rows, cols, k)
+    assert np.array_equal(ti, ti2) and 1234 not in ti.tolist()
+    ref, _ = orc.matvec(W, x, rows, cols)
+    assert math.isnan(orc.logsumexp(ref))
+
+
+def test_lmhead_probs_deterministic(q4k):
+    rng = np.random.default_rng(35)
+    rows, cols, k = 50000, 1024, 5
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols, scale=0.5)
+    a = gpu_lmhead_probs(q4k, W, x, rows, cols, k)
+    b = gpu_lmhead_probs(q4k, W, x, rows, cols, k)
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+    assert np.float32(a[4]).view(np.uint32) == np.float32(b[4]).view(np.uint32)
 
 
 # ----------------------------------------------------------------- prefill ---
