@@ -4,8 +4,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. It wraps ``q4k_oracle.c`` (plain C, f64,
 single-threaded) through ctypes and shares no code with the HIP library.
 
-Parity-unpinned parts: correspondence of the byte layout to Q4_K files written
-by other tools (no such file or decoder exists in this environment; the layout
+Parity-unpinned parts: correspondence of the byte layouts to Q4_K and Q6_K
+files written by other tools (no such file or decoder exists in this environment; the layout
 is pinned by round-trip, single-bit and closed-form tests instead).
 """
 from __future__ import annotations
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.q4o_act_array.argtypes = [P, I64, ctypes.c_int, P]
         L.q4o_ffn.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P, P, P, P]
         L.q4o_topk.argtypes = [P, I64, ctypes.c_int, P, P]
+        L.q6o_dequant_block.argtypes = [P, P]
+        L.q6o_dequant.argtypes = [P, I64, I64, P]
+        L.q6o_matvec.argtypes = [P, P, I64, I64, P, P]
         L.q4o_logsumexp.argtypes = [P, I64]
         L.q4o_logsumexp.restype = ctypes.c_double
         L.q4o_softmax.argtypes = [P, I64, P]
@@ -189,6 +192,44 @@ def topk(v, k: int):
     val = np.zeros(k, np.float64)
     lib().q4o_topk(_ptr(v), v.size, k, _ptr(idx), _ptr(val))
     return idx, val
+
+
+Q6K_BLOCK = 210
+
+
+def _check_w6(W: np.ndarray, rows: int, cols: int) -> None:
+    assert cols % 256 == 0, cols
+    assert W.dtype == np.uint8 and W.size == rows * (cols // 256) * Q6K_BLOCK, (W.shape, rows, cols)
+
+
+def q6k_dequant_block(blk) -> np.ndarray:
+    """The 256 weights of one 210-byte Q6_K block, f64."""
+    b = _u8(blk)
+    assert b.size == Q6K_BLOCK
+    w = np.zeros(256, np.float64)
+    lib().q6o_dequant_block(_ptr(b), _ptr(w))
+    return w
+
+
+def q6k_dequant(W, rows: int, cols: int) -> np.ndarray:
+    """Dense f64 [rows, cols] copy of a Q6_K matrix."""
+    W = _u8(W)
+    _check_w6(W, rows, cols)
+    out = np.zeros((rows, cols), np.float64)
+    lib().q6o_dequant(_ptr(W), rows, cols, _ptr(out))
+    return out
+
+
+def q6k_matvec(W, x, rows: int, cols: int):
+    """(y, A): y = W x in f64 for a Q6_K matrix, A = sum_j |w_ij x_j|."""
+    W = _u8(W)
+    _check_w6(W, rows, cols)
+    x = _f32(x)
+    assert x.size == cols
+    y = np.zeros(rows, np.float64)
+    A = np.zeros(rows, np.float64)
+    lib().q6o_matvec(_ptr(W), _ptr(x), rows, cols, _ptr(y), _ptr(A))
+    return y, A
 
 
 def logsumexp(v) -> float:

@@ -267,6 +267,67 @@ void q4o_topk(const double *v, int64_t n, int k, int64_t *idx, double *val)
     free(order);
 }
 
+/* ---- Q6_K: the other K-quant (GGUF super-block, 210 bytes / 256 weights) ----
+ * Sources: infer-compute README, "Shaders" table (q6k_matvec beside the Q4_K
+ * kernels) and "Design Principles" item 8 (Q4_K and Q6_K match the GGUF /
+ * Ollama quantisation). As for Q4_K the pages give no byte layout; it is the
+ * public GGUF Q6_K block: ql[128] (low 4 bits of each quant), qh[64] (high 2
+ * bits), scales[16] (signed 8-bit, one per 16 consecutive weights), then d
+ * (binary16) in bytes 208-209. Weight e = 128n + 32j + l (half n, quarter
+ * j, l = 0..31) has q = (nibble j/2 of ql[64n + 32(j%2) + l])
+ *                     | ((qh[32n + l] >> 2j) & 3) << 4,
+ * and w = d * scales[e/16] * (q - 32). Each w is exact in double (11 + 8 + 6
+ * significant bits). */
+#define Q6O_BLOCK 210
+
+static int q6o_quant(const uint8_t *blk, int e)
+{
+    const int n = e / 128, j = (e % 128) / 32, l = e % 32;
+    const uint8_t lo = blk[64 * n + 32 * (j % 2) + l];
+    const int low = (j / 2) ? (lo >> 4) : (lo & 0x0f);
+    const int high = (blk[128 + 32 * n + l] >> (2 * j)) & 3;
+    return low | (high << 4);
+}
+
+void q6o_dequant_block(const uint8_t *blk, double *w)
+{
+    const double d = q4o_f16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+    for (int e = 0; e < Q4O_QK; ++e) {
+        const int sc = (int8_t)blk[192 + e / 16];
+        w[e] = d * sc * (q6o_quant(blk, e) - 32);
+    }
+}
+
+void q6o_dequant(const uint8_t *W, int64_t rows, int64_t cols, double *out)
+{
+    const int64_t nb = cols / Q4O_QK;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t b = 0; b < nb; ++b)
+            q6o_dequant_block(W + (i * nb + b) * Q6O_BLOCK, out + i * cols + b * Q4O_QK);
+}
+
+/* y_i = sum_j w_ij x_j and A_i = sum_j |w_ij x_j| for a Q6_K matrix (either
+ * output may be NULL). */
+void q6o_matvec(const uint8_t *W, const float *x, int64_t rows, int64_t cols, double *y,
+                double *A)
+{
+    const int64_t nb = cols / Q4O_QK;
+    double w[Q4O_QK];
+    for (int64_t i = 0; i < rows; ++i) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            q6o_dequant_block(W + (i * nb + b) * Q6O_BLOCK, w);
+            for (int e = 0; e < Q4O_QK; ++e) {
+                const double t = w[e] * (double)x[b * Q4O_QK + e];
+                acc += t;
+                mag += fabs(t);
+            }
+        }
+        if (y) y[i] = acc;
+        if (A) A[i] = mag;
+    }
+}
+
 /* ---- softmax over all rows (the probability of a top-k prediction) ----
  * Source: infer-inference README, Overview example (the top prediction is
  * shown with its probability in percent); Performance -- infer-inference,

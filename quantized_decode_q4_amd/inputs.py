@@ -18,9 +18,18 @@ Random blocks use uniform bytes 4..143 (every 6-bit field and nibble is then an
 independent uniform integer) and d, dmin drawn uniformly from [1e-4, 2e-3) and
 rounded to binary16 by numpy (round-to-nearest-even).
 
+Q6_K block bytes (GGUF layout, 210 B per 256 weights):
+  bytes 0-127  : low 4 bits of the 256 quants
+  bytes 128-191: high 2 bits of the 256 quants
+  bytes 192-207: 16 signed 8-bit scales
+  bytes 208-209: d (IEEE binary16, little-endian)
+Random blocks use uniform bytes 0..207 (every quant and scale is then an
+independent uniform integer) and d drawn uniformly from [1e-4, 2e-3) and
+rounded to binary16.
+
 Seeding: numpy PCG64 via ``default_rng([0x51344B, config, tensor_id, index])``.
 Configs: 0 tiny matvec, 1 QKV, 2 FFN, 3 lm_head, 4 prefill activations, 5 the
-attention output projection.
+attention output projection, 6 Q6_K matvec at the down-projection shape.
 Tensor ids: 0 = W / Wqkv / Wg, 1 = Wu, 2 = Wd, 3 = x / X. ``index`` is the layer
 or copy number. Draw order inside ``q4k_random``: the 144-byte rows of raw bytes
 first, then all d values, then all dmin values (row-major over blocks).
@@ -30,7 +39,8 @@ from __future__ import annotations
 import numpy as np
 
 QK_K = 256            # weights per super-block
-BLOCK_BYTES = 144     # bytes per super-block
+BLOCK_BYTES = 144     # bytes per Q4_K super-block
+Q6K_BLOCK_BYTES = 210 # bytes per Q6_K super-block
 SEED_ROOT = 0x51344B
 
 # Shapes of the five workloads (rows, cols, ...)
@@ -67,6 +77,18 @@ def q4k_random(rng: np.random.Generator, rows: int, cols: int,
     raw[:, :, 0:2] = d.astype("<f2").view(np.uint8).reshape(rows, nb, 2)
     raw[:, :, 2:4] = dmin.astype("<f2").view(np.uint8).reshape(rows, nb, 2)
     return raw.reshape(rows, rb)
+
+
+def q6k_random(rng: np.random.Generator, rows: int, cols: int,
+               d_range=(D_LO, D_HI)) -> np.ndarray:
+    """Random Q6_K matrix as uint8[rows, cols/256*210] (row-major blocks)."""
+    if cols <= 0 or cols % QK_K:
+        raise ValueError(f"cols must be a positive multiple of {QK_K}, got {cols}")
+    nb = cols // QK_K
+    raw = rng.integers(0, 256, size=(rows, nb, Q6K_BLOCK_BYTES), dtype=np.uint8)
+    d = rng.uniform(d_range[0], d_range[1], size=(rows, nb)).astype(np.float16)
+    raw[:, :, 208:210] = d.astype("<f2").view(np.uint8).reshape(rows, nb, 2)
+    return raw.reshape(rows, nb * Q6K_BLOCK_BYTES)
 
 
 def normal_f32(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
@@ -113,6 +135,12 @@ def o_proj(layer: int = 0, hidden: int = HIDDEN, q_dim: int = Q_ROWS):
     """Attention output projection: W_o hidden x (8 heads x 256), input ~ N(0,1)."""
     return {"W": q4k_random(rng_for(5, 0, layer), hidden, q_dim),
             "x": normal_f32(rng_for(5, 3, layer), q_dim)}
+
+
+def q6k_down(layer: int = 0, hidden: int = HIDDEN, inter: int = INTER):
+    """Q6_K matvec at the FFN down-projection shape: W hidden x inter, x ~ N(0,1)."""
+    return {"W": q6k_random(rng_for(6, 0, layer), hidden, inter),
+            "x": normal_f32(rng_for(6, 3, layer), inter)}
 
 
 def prefill_x(seq: int = PREFILL_SEQ, hidden: int = HIDDEN, index: int = 0):

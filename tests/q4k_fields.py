@@ -89,3 +89,28 @@ class Fields:
         s = np.arange(256) // 32
         w = d * self.sc[:, :, s] * self.q - dmin * self.mn[:, :, s]
         return w.reshape(self.rows, self.cols)
+
+
+# ------------------------------------------------------------------ Q6_K ---
+
+def pack_q6k_block(d, scales, q) -> np.ndarray:
+    """210 bytes of one GGUF Q6_K block from its fields: 256 six-bit quants q
+    (0..63), 16 signed 8-bit scales (one per 16 consecutive weights) and d.
+    Quant e = 128n + 32j + l puts its low 4 bits in nibble j//2 of byte
+    64n + 32(j%2) + l and its high 2 bits in bits 2j..2j+1 of byte
+    128 + 32n + l; the scales fill bytes 192..207 and d bytes 208..209.
+    d is a float (rounded to binary16) or a numpy uint16 bit pattern."""
+    q = np.asarray(q, dtype=np.int64).reshape(256)
+    scales = np.asarray(scales, dtype=np.int64).reshape(16)
+    assert q.min() >= 0 and q.max() < 64
+    assert scales.min() >= -128 and scales.max() < 128
+    blk = np.zeros(210, np.uint8)
+    for e in range(256):
+        n, j, l = e // 128, (e % 128) // 32, e % 32
+        lo_byte = 64 * n + 32 * (j % 2) + l
+        blk[lo_byte] |= (q[e] & 0x0F) << (4 * (j // 2))
+        blk[128 + 32 * n + l] |= (q[e] >> 4) << (2 * j)
+    blk[192:208] = (scales & 0xFF).astype(np.uint8)
+    db = int(d) if isinstance(d, np.uint16) else f16_bits(d)
+    blk[208], blk[209] = db & 0xFF, db >> 8
+    return blk

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from q4k_fields import Fields, pack_block, pack_scales, pack_quants, f16_bits
+from q4k_fields import Fields, pack_block, pack_scales, pack_quants, f16_bits, pack_q6k_block
 from quantized_decode_q4_amd import inputs
 
 
@@ -372,6 +372,130 @@ def test_topk_duplicated_rows_lower_index_first(orc):
     y2, _ = orc.matvec(W2, x, rows, cols)
     idx, _ = orc.topk(y2, 3)
     assert idx.tolist()[:3] == sorted({best, 37, 150})[:3]
+
+
+# --------------------------------------------------------------------- Q6_K ---
+
+def test_q6k_block_round_trip_from_fields(orc):
+    """Blocks packed from random fields decode to d * scale[e // 16] * (q - 32)."""
+    rng = np.random.default_rng(51)
+    for _ in range(20):
+        q = rng.integers(0, 64, 256)
+        sc = rng.integers(-128, 128, 16)
+        d = float(np.float16(rng.uniform(1e-4, 2e-3)))
+        w = orc.q6k_dequant_block(pack_q6k_block(d, sc, q))
+        want = np.array([d * sc[e // 16] * (q[e] - 32) for e in range(256)], np.float64)
+        assert np.array_equal(w, want)
+
+
+def test_q6k_every_quant_bit_moves_exactly_one_weight(orc):
+    """From the all-zero-weight block (every q = 32, scales 1, d = 1), each of
+    the 1536 quant bits (bytes 0-191) changes exactly one weight, by a power of
+    two, and together they cover each of the 256 weights' six bits once."""
+    base = pack_q6k_block(1.0, np.ones(16, int), np.full(256, 32))
+    assert np.all(orc.q6k_dequant_block(base) == 0)
+    hits = {}
+    for byte in range(192):
+        for bit in range(8):
+            blk = base.copy()
+            blk[byte] ^= 1 << bit
+            w = orc.q6k_dequant_block(blk)
+            nz = np.flatnonzero(w)
+            assert nz.size == 1, (byte, bit)
+            e = int(nz[0])
+            mag = abs(w[e])
+            assert mag in (1, 2, 4, 8, 16, 32), (byte, bit, mag)
+            hits.setdefault(e, []).append(int(mag))
+    assert sorted(hits) == list(range(256))
+    assert all(sorted(v) == [1, 2, 4, 8, 16, 32] for v in hits.values())
+
+
+def test_q6k_scales_are_signed_and_cover_16_consecutive_weights(orc):
+    rng = np.random.default_rng(52)
+    q = rng.integers(0, 64, 256)
+    sc = np.ones(16, int)
+    w0 = orc.q6k_dequant_block(pack_q6k_block(1.0, sc, q))
+    for s in range(16):
+        for v in (-128, -1, 5, 127):
+            sc2 = sc.copy()
+            sc2[s] = v
+            w = orc.q6k_dequant_block(pack_q6k_block(1.0, sc2, q))
+            changed = np.flatnonzero(w != w0)
+            assert set(changed.tolist()) <= set(range(16 * s, 16 * s + 16))
+            assert np.array_equal(w[16 * s:16 * s + 16], v * w0[16 * s:16 * s + 16])
+    blk = pack_q6k_block(1.0, sc, q)
+    blk[192] = 0x80          # int8 -128
+    assert np.array_equal(orc.q6k_dequant_block(blk)[:16], -128 * w0[:16])
+
+
+def test_q6k_d_is_the_last_two_bytes(orc):
+    q = np.arange(256) % 64
+    sc = np.arange(16) - 8
+    blk = pack_q6k_block(0.5, sc, q)
+    w = orc.q6k_dequant_block(blk)
+    blk2 = blk.copy()
+    blk2[208:210] = np.array([f16_bits(-2.0) & 0xFF, f16_bits(-2.0) >> 8], np.uint8)
+    assert np.array_equal(orc.q6k_dequant_block(blk2), -4.0 * w)
+    # binary16 subnormal d
+    blk2[208:210] = np.array([0x01, 0x00], np.uint8)
+    assert np.array_equal(orc.q6k_dequant_block(blk2), w * (2.0 ** -24) / 0.5)
+
+
+def test_q6k_closed_forms(orc):
+    rows, cols = 3, 512
+    nb = cols // 256
+    x1 = np.ones(cols, np.float32)
+    # q = 32 everywhere: zero
+    W = np.stack([np.concatenate([pack_q6k_block(1e-3, np.full(16, 77), np.full(256, 32))
+                                  for _ in range(nb)]) for _ in range(rows)])
+    y, A = orc.q6k_matvec(W, x1, rows, cols)
+    assert np.all(y == 0) and np.all(A == 0)
+    # q = 63, scales 127, d = 1: every weight 127 * 31; sum of x = cols
+    W = np.stack([np.concatenate([pack_q6k_block(1.0, np.full(16, 127), np.full(256, 63))
+                                  for _ in range(nb)]) for _ in range(rows)])
+    y, A = orc.q6k_matvec(W, x1, rows, cols)
+    assert np.all(y == 127 * 31 * cols) and np.all(A == y)
+    # q = 0, scales -128: every weight (-128)(-32) = 4096
+    W = np.stack([np.concatenate([pack_q6k_block(0.25, np.full(16, -128), np.zeros(256, int))
+                                  for _ in range(nb)]) for _ in range(rows)])
+    x = np.random.default_rng(53).standard_normal(cols).astype(np.float32)
+    y, _ = orc.q6k_matvec(W, x, rows, cols)
+    assert np.allclose(y, 0.25 * 4096 * math.fsum(x.astype(np.float64)), rtol=1e-13, atol=1e-9)
+
+
+def test_q6k_matvec_one_hot_columns_and_linearity(orc):
+    rng = np.random.default_rng(54)
+    rows, cols = 40, 768
+    W = inputs.q6k_random(rng, rows, cols)
+    dense = orc.q6k_dequant(W, rows, cols)
+    for j in rng.choice(cols, 12, replace=False):
+        x = np.zeros(cols, np.float32)
+        x[j] = 1.0
+        y, A = orc.q6k_matvec(W, x, rows, cols)
+        assert np.array_equal(y, dense[:, j]) and np.array_equal(A, np.abs(dense[:, j]))
+    x1 = rng.standard_normal(cols).astype(np.float32)
+    x2 = rng.standard_normal(cols).astype(np.float32)
+    y1, _ = orc.q6k_matvec(W, x1, rows, cols)
+    y2, _ = orc.q6k_matvec(W, x2, rows, cols)
+    y12, _ = orc.q6k_matvec(W, (x1 + x2).astype(np.float32), rows, cols)
+    x12 = (x1 + x2).astype(np.float32).astype(np.float64)
+    assert np.allclose(y12, dense @ x12, rtol=1e-12, atol=1e-9)
+    assert np.allclose(y1 + y2, dense @ (x1.astype(np.float64) + x2), rtol=1e-12, atol=1e-9)
+
+
+def test_q6k_random_weight_moments(orc):
+    """Uniform bytes make q and the int8 scales uniform: E[q - 32] = -1/2,
+    E[scale] = -1/2, so E[w] = E[d] / 4, and E[w^2] = E[d^2] E[s^2] E[(q-32)^2]
+    with E[s^2] = 5461.5 and E[(q-32)^2] = 341.5."""
+    rng = np.random.default_rng(55)
+    rows, cols = 400, 2560
+    W = inputs.q6k_random(rng, rows, cols)
+    w = orc.q6k_dequant(W, rows, cols)
+    lo, hi = 1e-4, 2e-3
+    Ed, Ed2 = (lo + hi) / 2, (hi ** 3 - lo ** 3) / (3 * (hi - lo))
+    m1, m2 = w.mean(), (w ** 2).mean()
+    assert abs(m1 - Ed / 4) < 4 * math.sqrt(m2 / w.size) * 16    # blocks share d and scales
+    assert m2 == pytest.approx(Ed2 * 5461.5 * 341.5, rel=0.03)
 
 
 # ------------------------------------------------------------------ softmax ---
