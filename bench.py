@@ -9,8 +9,10 @@ step streams its weights from HBM. Steps are replayed from HIP graphs captured
 once (launch-bound inner loop); the eager launch rate is reported beside it.
 
 Beside the step: the full Q4_K sequence of a layer (QKV, the attention output
-projection 2560 x 2048, FFN) over the 34 layers, and the 64-token prefill FFN on the same 34 layers' weights (the
-matrix-core path) is timed per call and reported with its MFMA utilisation.
+projection 2560 x 2048, FFN) over the 34 layers; the Q6_K matvec at the
+down-projection shape (34 matrices in rotation); and the 64-token prefill FFN
+on the same 34 layers' weights (the matrix-core path), timed per call and
+reported with its MFMA utilisation.
 
 Prints ONE JSON line (see the fields at the end of main()).
 """
@@ -55,6 +57,8 @@ STEP_BYTES = LAYERS * LAYER_BYTES + LMHEAD_BYTES
 PREFILL_SEQ = 64
 PREFILL_BYTES = 3 * wbytes(INTER, HIDDEN) + 2 * PREFILL_SEQ * HIDDEN * 4
 PREFILL_FLOPS = 2 * PREFILL_SEQ * 3 * INTER * HIDDEN
+# Q6_K matvec at the down-projection shape: 210 bytes per 256 weights
+Q6K_BYTES = HIDDEN * (INTER // 256) * 210 + INTER * 4 + HIDDEN * 4
 
 
 def source_digest() -> str:
@@ -121,9 +125,10 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--kernel-only", default="", help="launch only this part (profiling): "
-                    "gate_up | down | qkv | lmhead | prefill | copy (a plain 1 GiB device "
+                    "gate_up | down | qkv | lmhead | prefill | q6k | copy (a plain 1 GiB device "
                     "copy that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill FFN leg")
+    ap.add_argument("--no-q6k", action="store_true", help="skip the Q6_K matvec leg")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -192,6 +197,18 @@ def main() -> int:
         Yp = torch.empty((PREFILL_SEQ, HIDDEN), device=dev)
         p_ws = q4k.workspace(q4k.q4k_ffn_prefill_workspace_bytes(PREFILL_SEQ, HIDDEN, INTER))
 
+    do_q6k = not args.no_q6k and args.kernel_only in ("", "q6k")
+    q6_dev = []
+    if do_q6k:
+        for l in range(LAYERS):
+            c6 = inputs.q6k_down(l)
+            q6_dev.append({"W": up(c6["W"]), "x": up(c6["x"])})
+        y6 = torch.empty(HIDDEN, device=dev)
+
+    def run_q6k():
+        for c6 in q6_dev:
+            q4k.q6k_matvec(c6["W"], c6["x"], y6, HIDDEN, INTER)
+
     def run_prefill():
         for l in range(LAYERS):
             L = ffn_dev[l]
@@ -234,6 +251,7 @@ def main() -> int:
                             for c in qkv_dev],
             "lmhead": run_lmhead,
             "prefill": run_prefill,
+            "q6k": run_q6k,
         }
         fn = parts[args.kernel_only]
         for i in range(args.warmup + args.steps):
@@ -368,6 +386,21 @@ def main() -> int:
     lm_plain_us = time_graph(run_lmhead_plain, 10)
     log(f"lm_head top-5: {lm_plain_us:.2f} us; with probabilities: {lm_probs_us:.2f} us")
 
+    # ----------------------------- Q6_K matvec at the down-projection shape
+    q6k_leg = None
+    if do_q6k:
+        q6_us = time_graph(run_q6k, 1) / LAYERS
+        q6_bytes = Q6K_BYTES
+        q6k_leg = {
+            "workload": "Q6_K matvec 2560x10240 (down-projection shape), 34 matrices in rotation, "
+                        "f32 activations",
+            "us_per_call": round(q6_us, 3),
+            "gbs": round(q6_bytes / (q6_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(q6_bytes / (q6_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_call": q6_bytes,
+        }
+        log(f"q6k matvec: {q6_us:.2f} us/call, {q6k_leg['gbs']:.0f} GB/s")
+
     # ------------------------------------------ prefill FFN (matrix cores)
     prefill = None
     if do_prefill:
@@ -460,6 +493,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "q6k_matvec": q6k_leg,
     }
     print(json.dumps(rec), flush=True)
     return 0

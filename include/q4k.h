@@ -78,7 +78,8 @@ enum q4k_act {
 };
 
 #define Q4K_QK 256            /* weights per super-block */
-#define Q4K_BLOCK_BYTES 144   /* bytes per super-block */
+#define Q4K_BLOCK_BYTES 144   /* bytes per Q4_K super-block */
+#define Q6K_BLOCK_BYTES 210   /* bytes per Q6_K super-block */
 #define Q4K_TOPK_MAX 64       /* largest k of q4k_lmhead_topk */
 #define Q4K_COLS_MAX 65536    /* largest cols (reduction length) */
 
@@ -86,6 +87,16 @@ enum q4k_act {
  * Source: infer-compute README, "Quick Start" (q4k_matvec) and "Shaders"
  * table (q4k_matvec). W: rows x cols Q4_K; x: f32[cols]; y: f32[rows]. */
 int q4k_matvec(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
+               void *stream);
+
+/* y[i] = sum_j W[i][j] * x[j] for a Q6_K matrix: rows x cols, each row
+ * cols/256 GGUF Q6_K blocks of 210 bytes (ql[128] low nibbles, qh[64] high
+ * bit pairs, 16 signed 8-bit scales, f16 d; w = d * scale * (q - 32), one
+ * scale per 16 consecutive weights). Blocks need not be aligned; W itself
+ * must be 16-byte aligned. x: f32[cols]; y: f32[rows]. f32 arithmetic.
+ * Source: infer-compute README, "Shaders" table (q6k_matvec) and "Design
+ * Principles" item 8 (Q6_K matches the GGUF/Ollama quantisation). */
+int q6k_matvec(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
                void *stream);
 
 /* Fused QKV projection: one pass over the concatenated rows [q; k; v] of Wqkv

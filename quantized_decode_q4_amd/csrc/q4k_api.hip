@@ -76,6 +76,21 @@ Q4K_EXPORT int q4k_matvec(const void *W, const float *x, float *y, int64_t rows,
                                              cols, rows, rows, as_stream(stream)));
 }
 
+Q4K_EXPORT int q6k_matvec(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
+                          void *stream)
+{
+    if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
+    if (rows == 0) return Q4K_OK;
+    if (!W || !x || !y) return Q4K_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_ERR_ALIGN;
+    const Span sy = span(y, rows * 4);
+    if (overlap(sy, span(W, rows * (cols / Q4K_QK) * Q6K_BLOCK_BYTES)) ||
+        overlap(sy, span(x, cols * 4)))
+        return Q4K_ERR_ALIAS;
+    return hip_status(q4k::launch_q6k_matvec((const uint8_t *)W, x, y, rows, cols,
+                                             as_stream(stream)));
+}
+
 Q4K_EXPORT int q4k_qkv(const void *Wqkv, const float *x, float *q, float *k, float *v,
                        int64_t q_rows, int64_t kv_rows, int64_t cols, void *stream)
 {

@@ -30,6 +30,9 @@ hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, 
 // down projection reading h.
 hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
                       float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s);
+// Q6_K matvec (GGUF Q6_K rows, 210 bytes per 256 weights): y = W x.
+hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t rows,
+                             int64_t cols, hipStream_t s);
 // lm_head: candidate-producing workgroups used on this device, and the most
 // any device uses for the shape (sizes the workspace).
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols);

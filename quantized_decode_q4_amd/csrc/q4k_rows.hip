@@ -35,9 +35,22 @@
 // v_dot4_i32_i8 for p2) on the raw nibbles, exact in 32-bit integers, scaled
 // by X_s once per sub-block. The min term uses the f32 sum of the sub-block's
 // activations. Non-finite activations make X_s NaN (outputs become NaN).
+//
+// Q6_K (the other K-quant of the Shaders table, q6k_matvec; GGUF block of
+// 210 bytes: ql[128], qh[64], 16 signed scales, f16 d) runs through the same
+// kernel with FMT_Q6K: unit g = 2n + h of a block holds the 64 weights
+// 128n + 32j + 16h + i (j = 0..3, i = 0..15), whose low nibbles are ql bytes
+// 64n + 16h + i (j = 0, 2) and 64n + 32 + 16h + i (j = 1, 3) and whose high
+// bit pairs are qh bytes 32n + 16h + i. Blocks are only 2-byte aligned, so each
+// field is read with 4-byte-aligned loads one dword wider and realigned in
+// registers (v_alignbyte); d is read with a 2-byte load, so no load reaches
+// past its block. Activations are f32: sum_i w_i x_i over a 16-weight
+// sub-block is d*sc*(sum_i q_i x_i - 32 sum_i x_i).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "q4k_internal.h"
 
@@ -69,6 +82,12 @@
 #ifndef Q4K_DOWN_WGS_PER_CU
 #define Q4K_DOWN_WGS_PER_CU 1
 #endif
+#ifndef Q6K_D
+#define Q6K_D 1                     // sweeps in flight, Q6_K matvec
+#endif
+#ifndef Q6K_WGS_PER_CU
+#define Q6K_WGS_PER_CU 1
+#endif
 #ifndef Q4K_LMHEAD_D
 #define Q4K_LMHEAD_D 1
 #endif
@@ -89,6 +108,11 @@ enum Epi { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_LOGITS = 3 };
 //            computes only a few rows, so that no conversion has to be paid
 //            for: the down projection of the FFN.
 enum XSrc { XS_LDS = 0, XS_THREAD = 1, XS_F32 = 3 };
+// Weight format of the rows.
+enum Fmt { FMT_Q4K = 0, FMT_Q6K = 1 };
+constexpr int kQ6Bytes = 210;   // bytes per Q6_K super-block
+
+__host__ __device__ constexpr int fmt_block_bytes(int fmt) { return fmt == FMT_Q6K ? kQ6Bytes : kBlockBytes; }
 
 struct RowsArgs {
     const uint8_t *W0;
@@ -161,6 +185,53 @@ __device__ __forceinline__ void load_slot(Slot<NMAT> &sl, const __amdgpu_buffer_
         sl.q[m][0] = q0.x; sl.q[m][1] = q0.y; sl.q[m][2] = q0.z; sl.q[m][3] = q0.w;
         sl.q[m][4] = q1.x; sl.q[m][5] = q1.y; sl.q[m][6] = q1.z; sl.q[m][7] = q1.w;
     }
+}
+
+// Q6_K: one in-flight row-unit per matrix, as loaded (4-byte aligned, one
+// dword wider than each field): ql of quarters 0/2 and 1/3 and qh (5 dwords
+// each), the 8 scale bytes of the half (3 dwords), d (16 bits), and the byte
+// misalignment of the block (0 or 2).
+template <int NMAT>
+struct Slot6 {
+    uint32_t q[NMAT][15];
+    uint32_t sc[NMAT][3];
+    uint32_t d[NMAT];
+    uint32_t mis;
+};
+
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0);
+}
+
+// off: byte offset of the block inside the (4-byte aligned) resource, or
+// kOutOfRange; n, h: the unit's half and 16-byte slice.
+template <int NMAT>
+__device__ __forceinline__ void load_slot6(Slot6<NMAT> &sl, const __amdgpu_buffer_rsrc_t (&rs)[NMAT],
+                                           uint32_t off, int n, int h)
+{
+    const uint32_t mis = off & 3u;      // 0 or 2 (blocks start at even bytes)
+    const uint32_t o = off - mis;       // kOutOfRange stays out of range
+    const uint32_t fa = o + 64u * n + 16u * h, fb = fa + 32u, fh = o + 128u + 32u * n + 16u * h;
+    const uint32_t fs = o + 192u + 8u * n;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        const uint4 a = bload16(rs[m], fa);
+        const uint4 b = bload16(rs[m], fb);
+        const uint4 c = bload16(rs[m], fh);
+        sl.q[m][0] = a.x; sl.q[m][1] = a.y; sl.q[m][2] = a.z; sl.q[m][3] = a.w;
+        sl.q[m][4] = bload4(rs[m], fa + 16u);
+        sl.q[m][5] = b.x; sl.q[m][6] = b.y; sl.q[m][7] = b.z; sl.q[m][8] = b.w;
+        sl.q[m][9] = bload4(rs[m], fb + 16u);
+        sl.q[m][10] = c.x; sl.q[m][11] = c.y; sl.q[m][12] = c.z; sl.q[m][13] = c.w;
+        sl.q[m][14] = bload4(rs[m], fh + 16u);
+        const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs[m], (int)fs, 0, 0);
+        sl.sc[m][0] = sv[0];
+        sl.sc[m][1] = sv[1];
+        sl.sc[m][2] = bload4(rs[m], fs + 8u);
+        sl.d[m] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs[m], (int)(off + 208u), 0, 0);
+    }
+    sl.mis = mis;
 }
 
 // ------------------------------------------------ block floating point ---
@@ -322,6 +393,57 @@ __device__ __forceinline__ float unit_dot_f32(const uint32_t (&nq)[8], uint4 hd,
     return fmaf(d, t1, -dmin * t2);
 }
 
+// Q6_K partial dot product of one unit of one row, f32 multiply-adds. The
+// thread's 64 activations are xf.xa = quarters 0, 1 and xf.xb = quarters 2,
+// 3 (16 each); s6[j] is the sum of quarter j's activations.
+__device__ __forceinline__ float unit_dot_q6(const uint32_t (&q)[15], const uint32_t (&sc)[3],
+                                             uint32_t dbits, uint32_t mis, const XF32 &xf,
+                                             const float (&s6)[4], int h)
+{
+    const uint32_t sh = mis;   // bytes to drop: 0 or 2
+    uint32_t qa[4], qb[4], qh[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        qa[k] = __builtin_amdgcn_alignbyte(q[k + 1], q[k], sh);
+        qb[k] = __builtin_amdgcn_alignbyte(q[k + 6], q[k + 5], sh);
+        qh[k] = __builtin_amdgcn_alignbyte(q[k + 11], q[k + 10], sh);
+    }
+    float acc[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        // six-bit quants of quarters 0..3 for l = 16h + 4k + c, c = byte
+        const uint32_t q0 = and_opaque(qa[k], 0x0F0F0F0Fu) | ((qh[k] << 4) & 0x30303030u);
+        const uint32_t q1 = and_opaque(qb[k], 0x0F0F0F0Fu) | ((qh[k] << 2) & 0x30303030u);
+        const uint32_t q2 = and_opaque(qa[k] >> 4, 0x0F0F0F0Fu) | (qh[k] & 0x30303030u);
+        const uint32_t q3 = and_opaque(qb[k] >> 4, 0x0F0F0F0Fu) | ((qh[k] >> 2) & 0x30303030u);
+        const uint32_t qj[4] = {q0, q1, q2, q3};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float *xj = j < 2 ? &xf.xa[16 * j] : &xf.xb[16 * (j - 2)];
+            acc[j][0] = fmaf((float)(qj[j] & 0xFFu), xj[4 * k + 0], acc[j][0]);
+            acc[j][1] = fmaf((float)((qj[j] >> 8) & 0xFFu), xj[4 * k + 1], acc[j][1]);
+            acc[j][0] = fmaf((float)((qj[j] >> 16) & 0xFFu), xj[4 * k + 2], acc[j][0]);
+            acc[j][1] = fmaf((float)(qj[j] >> 24), xj[4 * k + 3], acc[j][1]);
+        }
+    }
+    // scales of quarters j: bytes h + 2j of the half's 8 scale bytes
+    const uint32_t s03 = __builtin_amdgcn_alignbyte(sc[1], sc[0], sh);
+    const uint32_t s47 = __builtin_amdgcn_alignbyte(sc[2], sc[1], sh);
+    const int hs = 8 * h;
+    const float sc0 = (float)(int8_t)((s03 >> hs) & 0xFFu);
+    const float sc1 = (float)(int8_t)((s03 >> (hs + 16)) & 0xFFu);
+    const float sc2 = (float)(int8_t)((s47 >> hs) & 0xFFu);
+    const float sc3 = (float)(int8_t)((s47 >> (hs + 16)) & 0xFFu);
+    float t = sc0 * fmaf(-32.f, s6[0], acc[0][0] + acc[0][1]);
+    t = fmaf(sc1, fmaf(-32.f, s6[1], acc[1][0] + acc[1][1]), t);
+    t = fmaf(sc2, fmaf(-32.f, s6[2], acc[2][0] + acc[2][1]), t);
+    t = fmaf(sc3, fmaf(-32.f, s6[3], acc[3][0] + acc[3][1]), t);
+    const float d = __half2float(__ushort_as_half((unsigned short)(dbits & 0xFFFFu)));
+    return d * t;
+}
+
 // ------------------------------------------------------ wave reduction ---
 
 // Sum over the lanes of a wave that are congruent modulo RPS (every lane gets
@@ -461,15 +583,18 @@ __device__ __forceinline__ float block_sum_f32(float v, float *scratch)
 //  EPI  epilogue: store (3-way row split) / gated activation / logits + top-k
 //  XS   how the activations are held (see XSrc)
 //  D    sweeps whose loads are in flight while one sweep is computed
+//  FMT  weight format (Q4_K, or Q6_K with f32 activations)
 // Workgroup w processes the contiguous sweeps [S*w/G, S*(w+1)/G). The
 // activation loads and the quant/header loads of the first D sweeps are
 // issued first; then every step issues sweep i+D and computes sweep i. Wave
 // partial sums go to an LDS bank; every fb sweeps one barrier publishes them
 // and threads t < fb*RPS finish those rows.
-template <int RPS, int NMAT, int EPI, int XS, int MAXT, int D>
+template <int RPS, int NMAT, int EPI, int XS, int MAXT, int D, int FMT = FMT_Q4K>
 __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 {
     static_assert(RPS >= 1 && RPS <= 64 && (64 % RPS) == 0, "RPS must divide 64");
+    static_assert(FMT == FMT_Q4K || (XS == XS_F32 && NMAT == 1),
+                  "Q6_K: f32 activations, one matrix");
     constexpr int NW = MAXT / 64;
     constexpr int FB = Q4K_ROWS_FB;
     constexpr bool kInt = XS != XS_F32;
@@ -493,8 +618,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int sh = (g & 1) * 16;
     const bool upper = g >= 2;
     const int64_t cols = (int64_t)a.nb * kQK;
-    const int64_t rowbytes = (int64_t)a.nb * kBlockBytes;
-    const int64_t unit_off = (int64_t)b * kBlockBytes;
+    const int64_t rowbytes = (int64_t)a.nb * fmt_block_bytes(FMT);
+    const int64_t unit_off = (int64_t)b * fmt_block_bytes(FMT);
     const int64_t S = (a.rows + RPS - 1) / RPS;
     const int64_t s_begin = S * blockIdx.x / gridDim.x;
     const int64_t s_end = S * (blockIdx.x + 1) / gridDim.x;
@@ -502,17 +627,23 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int64_t row_stop = min(s_end * RPS, a.rows);
 
     // Buffer resources over this workgroup's rows (the host keeps the span
-    // below 2^30 bytes); offsets are relative to row_begin.
+    // below 2^30 bytes); offsets are relative to row_begin. Q6_K rows start at
+    // even bytes only: the resource then begins at the 4-byte boundary below
+    // (lead bytes of the previous row, never read as part of this one).
     __amdgpu_buffer_rsrc_t rs[NMAT];
+    uint32_t lead = 0;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-        rs[m] = make_rsrc((m == 0 ? a.W0 : a.W1) + row_begin * rowbytes,
-                          (uint32_t)((row_stop - row_begin) * rowbytes));
+    for (int m = 0; m < NMAT; ++m) {
+        const uint8_t *base = (m == 0 ? a.W0 : a.W1) + row_begin * rowbytes;
+        if (FMT == FMT_Q6K) lead = (uint32_t)((uintptr_t)base & 3u);
+        rs[m] = make_rsrc(base - lead, (uint32_t)((row_stop - row_begin) * rowbytes) + lead);
+    }
     const uint32_t qoff = 16u + 32u * (uint32_t)g;
     auto slot_off = [&](int64_t sw) -> uint32_t {
         const int64_t row = sw * RPS + r;
-        return (uact && row < row_stop) ? (uint32_t)((row - row_begin) * rowbytes + unit_off)
-                                        : kOutOfRange;
+        return (uact && row < row_stop)
+                   ? (uint32_t)((row - row_begin) * rowbytes + unit_off) + lead
+                   : kOutOfRange;
     };
 
     // ---- activation loads go out first, then the first D sweeps ----
@@ -526,18 +657,34 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         xv[0] = bload16(rx, xo);
         xv[1] = bload16(rx, xo + 16u);
     } else {
-        const uint32_t xo = uact ? (uint32_t)(64 * u) * 4u : kOutOfRange;
+        if (FMT == FMT_Q6K) {
+            // quarters j = 0..3 of unit (b, n, h): x[256b + 128n + 32j + 16h + i]
+            const uint32_t xo =
+                uact ? (uint32_t)(256 * b + 128 * (g >> 1) + 16 * (g & 1)) * 4u : kOutOfRange;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xo + 16u * i);
+            for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xo + 128u * (i / 4) + 16u * (i % 4));
+        } else {
+            const uint32_t xo = uact ? (uint32_t)(64 * u) * 4u : kOutOfRange;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xo + 16u * i);
+        }
     }
 
-    Slot<NMAT> buf[D + 1];
+    using SlotT = std::conditional_t<FMT == FMT_Q6K, Slot6<NMAT>, Slot<NMAT>>;
+    auto issue = [&](SlotT &sl, uint32_t off) {
+        if constexpr (FMT == FMT_Q6K)
+            load_slot6<NMAT>(sl, rs, off, g >> 1, g & 1);
+        else
+            load_slot<NMAT>(sl, rs, off, qoff);
+    };
+    SlotT buf[D + 1];
 #pragma unroll
-    for (int j = 0; j < D; ++j) load_slot<NMAT>(buf[j], rs, slot_off(s_begin + j), qoff);
+    for (int j = 0; j < D; ++j) issue(buf[j], slot_off(s_begin + j));
 
     // ---- the thread's activations (unused units: zeros) ----
     XUnit xu;
     XF32 xf;
+    float s6[4] = {0.f, 0.f, 0.f, 0.f};   // Q6_K: sums of the four quarters
     if (XS == XS_THREAD || XS == XS_F32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -555,6 +702,15 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             for (int i = 0; i < 32; ++i) {
                 xf.SA += xf.xa[i];
                 xf.SB += xf.xb[i];
+            }
+            if (FMT == FMT_Q6K) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float *xj = j < 2 ? &xf.xa[16 * j] : &xf.xb[16 * (j - 2)];
+                    s6[j] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s6[j] += xj[i];
+                }
             }
         }
     } else {
@@ -632,11 +788,15 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // One sweep: dot products, wave reduction, and every fb sweeps the
     // cross-wave reduction and epilogue of that batch of rows.
     int kb = 0, bank = 0;
-    auto compute_sweep = [&](const Slot<NMAT> &sl, int64_t sj) {
+    auto compute_sweep = [&](const SlotT &sl, int64_t sj) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-            float v = kInt ? unit_dot(sl.q[m], sl.h[m], xu, sh, upper)
-                           : unit_dot_f32(sl.q[m], sl.h[m], xf, sh, upper);
+            float v;
+            if constexpr (FMT == FMT_Q6K)
+                v = unit_dot_q6(sl.q[m], sl.sc[m], sl.d[m], sl.mis, xf, s6, g & 1);
+            else
+                v = kInt ? unit_dot(sl.q[m], sl.h[m], xu, sh, upper)
+                         : unit_dot_f32(sl.q[m], sl.h[m], xf, sh, upper);
             v = wave_sum_mod<RPS>(v);
             if (lane < RPS) red[bank][wave][(kb * NMAT + m) * RPS + lane] = v;
         }
@@ -681,8 +841,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     for (; s + D < s_end; s += D + 1) {
 #pragma unroll
         for (int j = 0; j <= D; ++j) {
-            if (D > 0) load_slot<NMAT>(buf[(j + D) % (D + 1)], rs, slot_off(s + j + D), qoff);
-            if (D == 0) load_slot<NMAT>(buf[0], rs, slot_off(s + j), qoff);
+            if (D > 0) issue(buf[(j + D) % (D + 1)], slot_off(s + j + D));
+            if (D == 0) issue(buf[0], slot_off(s + j));
             compute_sweep(buf[j], s + j);
         }
     }
@@ -690,7 +850,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 #pragma unroll
     for (int j = 0; j < (D > 0 ? D : 1); ++j) {
         if (s + j < s_end) {
-            if (D == 0) load_slot<NMAT>(buf[0], rs, slot_off(s + j), qoff);
+            if (D == 0) issue(buf[0], slot_off(s + j));
             compute_sweep(buf[j], s + j);
         }
     }
@@ -879,7 +1039,7 @@ int device_cus()
     return cache[dev];
 }
 
-template <int NMAT, int EPI, int XS, int D>
+template <int NMAT, int EPI, int XS, int D, int FMT = FMT_Q4K>
 hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s)
 {
     const dim3 grid((unsigned)nwg), block((unsigned)threads);
@@ -887,14 +1047,14 @@ hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hip
     const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols) : 0;
     if (threads > 512) {
         // only reachable with one row per sweep (cols > 32768: no LDS planes)
-        hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, XS == XS_LDS ? XS_THREAD : XS, 1024, 0>),
+        hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, XS == XS_LDS ? XS_THREAD : XS, 1024, 0, FMT>),
                            grid, block, 0, s, a);
         return hipGetLastError();
     }
     switch (rps) {
 #define Q4K_RPS_CASE(R)                                                                       \
     case R:                                                                                   \
-        hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, XS, 512, D>), grid, block, lds, s, a); \
+        hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, XS, 512, D, FMT>), grid, block, lds, s, a); \
         break;
         Q4K_RPS_CASE(1)
         Q4K_RPS_CASE(2)
@@ -933,11 +1093,12 @@ RowsArgs base_args(int64_t rows, int64_t cols)
 // Grid: about `per_cu` workgroups per compute unit, never more than there are
 // sweeps, and enough that one workgroup's rows span less than 2^30 bytes (its
 // buffer resource uses 32-bit offsets).
-int64_t grid_for(int64_t rows, int64_t cols, const Shape &sh, int per_cu)
+int64_t grid_for(int64_t rows, int64_t cols, const Shape &sh, int per_cu,
+                 int block_bytes = kBlockBytes)
 {
     const int64_t S = (rows + sh.rps - 1) / sh.rps;
     int64_t g = (int64_t)device_cus() * per_cu;
-    const int64_t sweep_bytes = (int64_t)sh.rps * (cols / kQK) * kBlockBytes;
+    const int64_t sweep_bytes = (int64_t)sh.rps * (cols / kQK) * block_bytes;
     int64_t max_sweeps = ((int64_t)1 << 30) / sweep_bytes;
     if (max_sweeps < 2) max_sweeps = 2;
     const int64_t min_g = (S + max_sweeps - 2) / (max_sweeps - 1);
@@ -999,6 +1160,18 @@ hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, c
     const Shape sd = pick_shape(inter);
     return launch_rows<1, EPI_STORE, XS_F32, Q4K_DOWN_D>(
         b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s);
+}
+
+hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t rows,
+                             int64_t cols, hipStream_t s)
+{
+    RowsArgs a = base_args(rows, cols);
+    a.W0 = W;
+    a.x = x;
+    a.o0 = y;
+    const Shape sh = pick_shape(cols);
+    const int64_t nwg = grid_for(rows, cols, sh, Q6K_WGS_PER_CU, kQ6Bytes);
+    return launch_rows<1, EPI_STORE, XS_F32, Q6K_D, FMT_Q6K>(a, sh.rps, sh.threads, nwg, s);
 }
 
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols)

@@ -53,6 +53,7 @@ _SIGS = {
     "q4k_ffn": ([_P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P], _INT),
     "q4k_lmhead_workspace_bytes": ([_I64, _I64, _INT], _SZ),
     "q4k_lmhead_topk": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _SZ, _P], _INT),
+    "q6k_matvec": ([_P, _P, _P, _I64, _I64, _P], _INT),
     "q4k_lmhead_topk_probs": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P, _P, _SZ, _P], _INT),
     "q4k_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4k_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
@@ -104,6 +105,10 @@ def _check(status: int, where: str) -> None:
 
 def q4k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
     _check(lib.q4k_matvec(_ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)), "q4k_matvec")
+
+
+def q6k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
+    _check(lib.q6k_matvec(_ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)), "q6k_matvec")
 
 
 def q4k_qkv(Wqkv, x, q, k, v, q_rows: int, kv_rows: int, cols: int, stream=None) -> None:

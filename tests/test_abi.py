@@ -21,7 +21,7 @@ S = None  # stream
 def declared_functions():
     text = open(q4k.HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q4k_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q[46]k_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -103,6 +103,20 @@ def test_gate_up_and_ffn_validation():
     assert L.q4k_ffn(A, B, C, D, E, 256, 512, 5, F, need, S) == q4k.Q4K_ERR_ACT
     assert L.q4k_ffn(A, B, C, D, F, 256, 512, 0, F, need, S) == q4k.Q4K_ERR_ALIAS   # y in ws
     assert L.q4k_ffn(A, B, C, D, E, 256, 512, 0, D, need, S) == q4k.Q4K_ERR_ALIAS   # ws on x
+
+
+def test_q6k_matvec_validation():
+    P = L.q6k_matvec
+    assert P(A, B, C, 10, 300, S) == q4k.Q4K_ERR_SHAPE
+    assert P(A, B, C, -1, 256, S) == q4k.Q4K_ERR_SHAPE
+    assert P(A, B, C, 10, 65536 + 256, S) == q4k.Q4K_ERR_SHAPE
+    assert P(None, B, C, 10, 256, S) == q4k.Q4K_ERR_NULL
+    assert P(A + 2, B, C, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert P(A, B + 4, C, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert P(A, B, C + 2, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert P(A, B, A + 2096, 10, 256, S) == q4k.Q4K_ERR_ALIAS   # y inside W (10 x 210 B)
+    assert P(A, B, B + 512, 10, 256, S) == q4k.Q4K_ERR_ALIAS    # y inside x
+    assert P(None, None, None, 0, 256, S) == q4k.Q4K_OK         # rows = 0: nothing to do
 
 
 def test_lmhead_validation():
