@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.q4o_act_array.argtypes = [P, I64, ctypes.c_int, P]
         L.q4o_ffn.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P, P, P, P]
         L.q4o_topk.argtypes = [P, I64, ctypes.c_int, P, P]
+        L.q4o_ffn_f64.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P, P, P, P]
+        L.q4o_residual_rmsnorm.argtypes = [P, P, P, ctypes.c_float, I64, P, P]
         L.q6o_dequant_block.argtypes = [P, P]
         L.q6o_dequant.argtypes = [P, I64, I64, P]
         L.q6o_matvec.argtypes = [P, P, I64, I64, P, P]
@@ -182,6 +184,39 @@ def ffn(Wg, Wu, Wd, x, hidden: int, inter: int, act: int = GELU_TANH):
     lib().q4o_ffn(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(x), hidden, inter, int(act),
                   _ptr(y), _ptr(A), _ptr(g), _ptr(u), _ptr(h))
     return {"y": y, "A": A, "g": g, "u": u, "h": h}
+
+
+def ffn_f64(Wg, Wu, Wd, x, hidden: int, inter: int, act: int = GELU_TANH):
+    """q4o_ffn with an f64 activation vector (e.g. a normalised residual)."""
+    Wg, Wu, Wd = _u8(Wg), _u8(Wu), _u8(Wd)
+    _check_w(Wg, inter, hidden)
+    _check_w(Wu, inter, hidden)
+    _check_w(Wd, hidden, inter)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    assert x.size == hidden
+    y = np.zeros(hidden, np.float64)
+    A = np.zeros(hidden, np.float64)
+    g = np.zeros(inter, np.float64)
+    u = np.zeros(inter, np.float64)
+    h = np.zeros(inter, np.float64)
+    lib().q4o_ffn_f64(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(x), hidden, inter, int(act),
+                      _ptr(y), _ptr(A), _ptr(g), _ptr(u), _ptr(h))
+    return {"y": y, "A": A, "g": g, "u": u, "h": h}
+
+
+def residual_rmsnorm(h, delta, w, eps: float):
+    """(s f32, x f64): s = h + delta in f32 (delta None: s = h),
+    x = s / sqrt(mean(s^2) + eps) * w in f64."""
+    h = _f32(h)
+    w = _f32(w)
+    n = h.size
+    assert w.size == n
+    d = None if delta is None else _f32(delta)
+    s = np.zeros(n, np.float32)
+    x = np.zeros(n, np.float64)
+    lib().q4o_residual_rmsnorm(_ptr(h), None if d is None else _ptr(d), _ptr(w),
+                               ctypes.c_float(eps), n, _ptr(s), _ptr(x))
+    return s, x
 
 
 def topk(v, k: int):

@@ -163,15 +163,15 @@ void q4o_act_array(const double *z, int64_t n, int act, double *out)
  *   g = Wg x, u = Wu x (Wg, Wu: inter x hidden), h = act(g) * u,
  *   y = Wd h (Wd: hidden x inter), A = sum_j |wd_ij h_j| with this h.
  * act: 0 = GELU-tanh, 1 = SiLU. g, u, h, A may be NULL. */
-void q4o_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
-             int64_t hidden, int64_t inter, int act,
-             double *y, double *A, double *g_out, double *u_out, double *h_out)
+void q4o_ffn_f64(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const double *x,
+                 int64_t hidden, int64_t inter, int act,
+                 double *y, double *A, double *g_out, double *u_out, double *h_out)
 {
     double *g = (double *)malloc((size_t)inter * sizeof(double));
     double *u = (double *)malloc((size_t)inter * sizeof(double));
     double *h = (double *)malloc((size_t)inter * sizeof(double));
-    q4o_matvec(Wg, x, inter, hidden, g, NULL);
-    q4o_matvec(Wu, x, inter, hidden, u, NULL);
+    q4o_matvec_f64(Wg, x, inter, hidden, g, NULL);
+    q4o_matvec_f64(Wu, x, inter, hidden, u, NULL);
     for (int64_t i = 0; i < inter; ++i)
         h[i] = (act == 0 ? q4o_gelu_tanh(g[i]) : q4o_silu(g[i])) * u[i];
     q4o_matvec_f64(Wd, h, hidden, inter, y, A);
@@ -181,6 +181,40 @@ void q4o_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const floa
     free(g);
     free(u);
     free(h);
+}
+
+/* The same with an f32 activation vector (widened exactly). */
+void q4o_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
+             int64_t hidden, int64_t inter, int act,
+             double *y, double *A, double *g_out, double *u_out, double *h_out)
+{
+    double *xd = (double *)malloc((size_t)hidden * sizeof(double));
+    for (int64_t j = 0; j < hidden; ++j) xd[j] = (double)x[j];
+    q4o_ffn_f64(Wg, Wu, Wd, xd, hidden, inter, act, y, A, g_out, u_out, h_out);
+    free(xd);
+}
+
+/* ---- RMSNorm of the residual stream, the step before a projection ----
+ * Sources: infer-compute README, "Key Optimizations" table (cooperative
+ * rms_norm / residual_norm) and "Shaders" table (fused residual_norm);
+ * Performance -- infer-inference, "Norm comparison" table (RMSNorm).
+ * The residual stream is f32: s = h + delta is one IEEE single addition
+ * (delta may be NULL: s = h). Then, in double,
+ *   x_j = s_j / sqrt(mean_k(s_k^2) + eps) * w_j,
+ * w the norm's weight vector (a model whose norm scales by 1 + w passes
+ * 1 + w). s_out (f32) and x_out (f64) receive s and x. */
+void q4o_residual_rmsnorm(const float *h, const float *delta, const float *w, float eps,
+                          int64_t n, float *s_out, double *x_out)
+{
+    double ss = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        const float a = h[j], b = delta ? delta[j] : 0.0f;
+        const float sj = delta ? a + b : a;   /* one f32 rounding */
+        s_out[j] = sj;
+        ss += (double)sj * (double)sj;
+    }
+    const double inv = 1.0 / sqrt(ss / (double)n + (double)eps);
+    for (int64_t j = 0; j < n; ++j) x_out[j] = (double)s_out[j] * inv * (double)w[j];
 }
 
 /* Derivatives of the activations, written from their definitions:

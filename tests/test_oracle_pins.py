@@ -498,6 +498,93 @@ def test_q6k_random_weight_moments(orc):
     assert m2 == pytest.approx(Ed2 * 5461.5 * 341.5, rel=0.03)
 
 
+# ------------------------------------------------------------------ RMSNorm ---
+
+def test_residual_add_is_one_f32_addition(orc):
+    rng = np.random.default_rng(71)
+    h = (rng.standard_normal(4096) * 100).astype(np.float32)
+    d = (rng.standard_normal(4096) * 1e-3).astype(np.float32)
+    h[:4] = [1.0, -1.0, 3e38, 1e-30]
+    d[:4] = [2.0 ** -30, 2.0 ** -25, 3e38, -1e-30]
+    s, _ = orc.residual_rmsnorm(h, d, np.ones(4096, np.float32), 1e-6)
+    with np.errstate(over="ignore"):
+        want = h + d      # numpy: IEEE single addition, round to nearest even (3e38 + 3e38 = inf)
+    assert np.array_equal(s.view(np.uint32), want.view(np.uint32))
+    s0, x0 = orc.residual_rmsnorm(h, None, np.ones(4096, np.float32), 1e-6)
+    s1, x1 = orc.residual_rmsnorm(h, np.zeros(4096, np.float32), np.ones(4096, np.float32), 1e-6)
+    assert np.array_equal(s0, h) and np.array_equal(x0, x1)
+
+
+def test_rmsnorm_unit_weight_has_unit_rms(orc):
+    rng = np.random.default_rng(72)
+    for n in (256, 2560, 10240):
+        h = (rng.standard_normal(n) * 7.5).astype(np.float32)
+        _, x = orc.residual_rmsnorm(h, None, np.ones(n, np.float32), 0.0)
+        assert math.fsum(x * x) / n == pytest.approx(1.0, abs=1e-12)   # f64 sum over n terms
+        assert np.all(np.sign(x) == np.sign(h))
+
+
+def test_rmsnorm_scale_invariance_and_weights(orc):
+    """eps = 0: multiplying s by a power of two (exact in f32) leaves x
+    unchanged, -1 flips it, and the weight multiplies element by element."""
+    rng = np.random.default_rng(73)
+    n = 2560
+    h = rng.standard_normal(n).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+    _, x = orc.residual_rmsnorm(h, None, w, 0.0)
+    for c in (2.0 ** 20, 2.0 ** -20, -1.0):
+        _, xc = orc.residual_rmsnorm((h * np.float32(c)).astype(np.float32), None, w, 0.0)
+        assert np.allclose(xc, np.sign(c) * x, rtol=1e-14, atol=0)
+    _, x1 = orc.residual_rmsnorm(h, None, np.ones(n, np.float32), 0.0)
+    assert np.allclose(x, x1 * w.astype(np.float64), rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_closed_forms(orc):
+    n = 1000
+    w = np.linspace(0.5, 1.5, n).astype(np.float32)
+    # constant vector c: x_j = w_j c / sqrt(c^2 + eps)
+    for c, eps in [(3.0, 0.0), (-0.25, 1e-6), (1e-3, 1e-6)]:
+        _, x = orc.residual_rmsnorm(np.full(n, c, np.float32), None, w, eps)
+        cf = float(np.float32(c))
+        want = w.astype(np.float64) * cf / math.sqrt(cf * cf + float(np.float32(eps)))
+        assert np.allclose(x, want, rtol=1e-14, atol=0)
+    # one nonzero element a at k, eps = 0: x_k = sign(a) sqrt(n) w_k, others 0
+    h = np.zeros(n, np.float32)
+    h[123] = -7.0
+    _, x = orc.residual_rmsnorm(h, None, w, 0.0)
+    assert x[123] == pytest.approx(-math.sqrt(n) * float(w[123]), rel=1e-15)
+    assert np.count_nonzero(x) == 1
+    # zero input with eps > 0 stays zero
+    _, x = orc.residual_rmsnorm(np.zeros(n, np.float32), None, w, 1e-6)
+    assert np.all(x == 0)
+
+
+def test_rmsnorm_then_matvec_one_hot(orc):
+    """A one-element residual normalises to sqrt(n) e_k (eps = 0, w = 1), so the
+    following matvec reads sqrt(n) times column k of the weights."""
+    rng = np.random.default_rng(74)
+    rows, cols = 64, 512
+    W = inputs.q4k_random(rng, rows, cols)
+    h = np.zeros(cols, np.float32)
+    h[300] = 0.5
+    _, x = orc.residual_rmsnorm(h, None, np.ones(cols, np.float32), 0.0)
+    y, _ = orc.matvec_f64(W, x, rows, cols)
+    col = orc.dequant(W, rows, cols)[:, 300]
+    assert np.allclose(y, math.sqrt(cols) * col, rtol=1e-14, atol=1e-300)
+
+
+def test_ffn_f64_matches_ffn_on_f32_inputs(orc):
+    rng = np.random.default_rng(75)
+    hidden, inter = 256, 512
+    Wg = inputs.q4k_random(rng, inter, hidden)
+    Wu = inputs.q4k_random(rng, inter, hidden)
+    Wd = inputs.q4k_random(rng, hidden, inter)
+    x = rng.standard_normal(hidden).astype(np.float32)
+    a = orc.ffn(Wg, Wu, Wd, x, hidden, inter, 0)
+    b = orc.ffn_f64(Wg, Wu, Wd, x.astype(np.float64), hidden, inter, 0)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["A"], b["A"])
+
+
 # ------------------------------------------------------------------ softmax ---
 
 def test_softmax_two_values_is_the_logistic_function(orc):
