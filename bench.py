@@ -229,6 +229,26 @@ def main() -> int:
             q4k.q4k_matvec(o["W"], o["x"], yo, HIDDEN, QROWS)
             q4k.q4k_ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], y, HIDDEN, INTER, GELU, h)
 
+    # residual stream for the layer sequence with the norms fused (double-buffered)
+    if o_dev:
+        nrm = [inputs.norm_inputs(i) for i in range(2)]
+        h_cur, h_mid = up(nrm[0]["h"]), torch.empty(HIDDEN, device=dev)
+        w_attn, w_ffn = up(nrm[0]["w"]), up(nrm[1]["w"])
+        f_y = torch.zeros(HIDDEN, device=dev)
+        qkv_y = torch.empty(QROWS + 2 * KVROWS, device=dev)
+        EPS = nrm[0]["eps"]
+
+    def run_norm_layers():
+        # per layer: norm(h + ffn_out) -> QKV, O projection, norm(h + o) -> FFN;
+        # the stream h is carried from layer to layer
+        for l in range(LAYERS):
+            c, o, L = qkv_dev[l], o_dev[l], ffn_dev[l]
+            q4k.q4k_rmsnorm_matvec(c["W"], h_cur, f_y, w_attn, EPS, h_mid, qkv_y,
+                                   QROWS + 2 * KVROWS, HIDDEN)
+            q4k.q4k_matvec(o["W"], o["x"], yo, HIDDEN, QROWS)
+            q4k.q4k_rmsnorm_ffn(L["Wg"], L["Wu"], L["Wd"], h_mid, yo, w_ffn, EPS, h_cur, f_y,
+                                HIDDEN, INTER, GELU, h)
+
     def run_lmhead():
         q4k.q4k_lmhead_topk_probs(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx,
                                   top_val, top_prob, lse, lm_ws)
@@ -278,6 +298,26 @@ def main() -> int:
         step_layers, step_lm = run_layers, run_lmhead
 
     stream = torch.cuda.current_stream()
+
+    def time_graph(fn, n):
+        # median of 3 replays of a graph of n calls of fn, in us per call
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            g.replay()
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a_ev.elapsed_time(b_ev) * 1e3 / n)
+        return sorted(ts)[1]
+
     for _ in range(args.warmup):
         step_layers()
         step_lm()
@@ -358,26 +398,10 @@ def main() -> int:
     full_ms.sort()
     us_full_layer = full_ms[len(full_ms) // 2] * 1e3 / LAYERS
     log(f"full layer (QKV + O + FFN): {us_full_layer:.2f} us")
+    us_norm_layer = time_graph(run_norm_layers, 1) / LAYERS
+    log(f"full layer with the two RMSNorms fused: {us_norm_layer:.2f} us")
 
     # ------------- lm_head: cost of the softmax probabilities beside top-k
-    def time_graph(fn, n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(n):
-                fn()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(3):
-            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_ev.record(stream)
-            g.replay()
-            b_ev.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a_ev.elapsed_time(b_ev) * 1e3 / n)
-        return sorted(ts)[1]
-
     def run_lmhead_plain():
         q4k.q4k_lmhead_topk(lm_dev["W"], lm_dev["x"], logits, VOCAB, HIDDEN, TOPK, top_idx, top_val,
                             lm_ws)
@@ -475,6 +499,7 @@ def main() -> int:
         "decode_layer_gbs": round(LAYER_BYTES / (us_per_layer * 1e-6) / 1e9, 1),
         "us_per_full_layer": round(us_full_layer, 3),
         "full_layer_gbs": round((LAYER_BYTES + O_BYTES) / (us_full_layer * 1e-6) / 1e9, 1),
+        "us_per_full_layer_fused_norms": round(us_norm_layer, 3),
         "lm_head_us": round(med_lm_ms * 1e3, 2),
         "lm_head_gbs": round(LMHEAD_BYTES / (med_lm_ms * 1e-3) / 1e9, 1),
         "lm_head_topk_only_us": round(lm_plain_us, 2),

@@ -69,7 +69,8 @@ enum q4k_status {
     Q4K_ERR_ACT = -5,       /* unknown activation */
     Q4K_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required */
     Q4K_ERR_ALIAS = -7,     /* an output overlaps an input or another output */
-    Q4K_ERR_HIP = -8        /* a HIP runtime/launch error */
+    Q4K_ERR_HIP = -8,       /* a HIP runtime/launch error */
+    Q4K_ERR_EPS = -9        /* a norm's eps negative or not finite */
 };
 
 enum q4k_act {
@@ -122,6 +123,33 @@ size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter);
  * followed by q4k_geglu_gelu_tanh_down / q4k_geglu_silu_down). */
 int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
             int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes, void *stream);
+
+/* Residual RMSNorm fused into a projection's input (the residual_norm step
+ * before a layer's projections):
+ *   s = h + delta   (f32 addition; delta may be NULL: s = h),
+ *   x = s / sqrt(mean(s^2) + eps) * norm_w,   y = W x.
+ * h, delta, norm_w: f32[cols]; h_out (may be NULL) receives s, the updated
+ * residual stream, and must not overlap any other argument (in particular not
+ * h: other workgroups still read h while it is written). A model whose norm
+ * scales by (1 + w) passes 1 + w as norm_w. The scalar 1/sqrt(...) is applied
+ * to each output row; (s * norm_w) is what the weights multiply. eps must be
+ * finite and >= 0 (else Q4K_ERR_EPS); rows must be >= 1. For a fused QKV
+ * projection pass Wqkv with rows = q_rows + 2*kv_rows: q, k, v are then the
+ * consecutive slices of y. h, delta, norm_w, h_out: 16-byte aligned.
+ * Source: infer-compute README, "Key Optimizations" table (cooperative
+ * rms_norm / residual_norm) and "Shaders" table (fused residual_norm);
+ * Performance -- infer-inference, "Norm comparison" table (RMSNorm). */
+int q4k_rmsnorm_matvec(const void *W, const float *h, const float *delta, const float *norm_w,
+                       float eps, float *h_out, float *y, int64_t rows, int64_t cols,
+                       void *stream);
+
+/* q4k_ffn with the same residual RMSNorm fused into the gate+up input
+ * (hidden = the norm's length); the down projection reads h as in q4k_ffn.
+ * Workspace: q4k_ffn_workspace_bytes. */
+int q4k_rmsnorm_ffn(const void *Wg, const void *Wu, const void *Wd, const float *h,
+                    const float *delta, const float *norm_w, float eps, float *h_out, float *y,
+                    int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes,
+                    void *stream);
 
 /* Workspace of q4k_lmhead_topk and q4k_lmhead_topk_probs: per-workgroup
  * top-k candidates and softmax partials. */

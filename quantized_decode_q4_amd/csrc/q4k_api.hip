@@ -56,6 +56,7 @@ Q4K_EXPORT const char *q4k_status_string(int status)
         case Q4K_ERR_WORKSPACE: return "Q4K_ERR_WORKSPACE: workspace NULL or too small";
         case Q4K_ERR_ALIAS: return "Q4K_ERR_ALIAS: an output overlaps an input or another output";
         case Q4K_ERR_HIP: return "Q4K_ERR_HIP: HIP runtime error (see q4k_last_hip_error)";
+        case Q4K_ERR_EPS: return "Q4K_ERR_EPS: eps must be finite and >= 0";
         default: return "unknown q4k status";
     }
 }
@@ -159,6 +160,78 @@ Q4K_EXPORT int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const flo
     return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                       (const uint8_t *)Wd, x, y, hidden, inter, act,
                                       (float *)ws, as_stream(stream)));
+}
+
+// ------------------------------------------------ fused residual RMSNorm ---
+
+static bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.402823466e38f; }  // NaN fails
+
+// Checks shared by the norm entry points: the norm inputs h, delta (optional),
+// w (cols floats each) and the optional new stream h_out; `outs` are the
+// call's other outputs, `ins` its weights. h_out may overlap nothing.
+static int norm_checks(const float *h, const float *delta, const float *w, float eps,
+                       float *h_out, int64_t cols, const Span *ins, int nins, const Span *outs,
+                       int nouts)
+{
+    if (!h || !w) return Q4K_ERR_NULL;
+    if (!eps_ok(eps)) return Q4K_ERR_EPS;
+    if (!aligned(h, 16) || !aligned(delta, 16) || !aligned(w, 16) || !aligned(h_out, 16))
+        return Q4K_ERR_ALIGN;
+    const Span nin[3] = {span(h, cols * 4), span(delta, delta ? cols * 4 : 0), span(w, cols * 4)};
+    const Span so = span(h_out, h_out ? cols * 4 : 0);
+    for (int j = 0; j < 3; ++j) {
+        if (overlap(so, nin[j])) return Q4K_ERR_ALIAS;
+        for (int i = 0; i < nouts; ++i)
+            if (overlap(outs[i], nin[j])) return Q4K_ERR_ALIAS;
+    }
+    for (int j = 0; j < nins; ++j)
+        if (overlap(so, ins[j])) return Q4K_ERR_ALIAS;
+    for (int i = 0; i < nouts; ++i)
+        if (overlap(so, outs[i])) return Q4K_ERR_ALIAS;
+    return Q4K_OK;
+}
+
+Q4K_EXPORT int q4k_rmsnorm_matvec(const void *W, const float *h, const float *delta,
+                                  const float *norm_w, float eps, float *h_out, float *y,
+                                  int64_t rows, int64_t cols, void *stream)
+{
+    if (!rows_ok(rows) || !cols_ok(cols) || rows == 0) return Q4K_ERR_SHAPE;
+    if (!W || !y) return Q4K_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(y, 4)) return Q4K_ERR_ALIGN;
+    const Span sw = span(W, wbytes(rows, cols)), sy = span(y, rows * 4);
+    if (overlap(sy, sw)) return Q4K_ERR_ALIAS;
+    const int c = norm_checks(h, delta, norm_w, eps, h_out, cols, &sw, 1, &sy, 1);
+    if (c != Q4K_OK) return c;
+    const q4k::NormIn n = {delta, norm_w, eps, h_out};
+    return hip_status(q4k::launch_rows_store((const uint8_t *)W, h, y, nullptr, nullptr, rows,
+                                             cols, rows, rows, as_stream(stream), &n));
+}
+
+Q4K_EXPORT int q4k_rmsnorm_ffn(const void *Wg, const void *Wu, const void *Wd, const float *h,
+                               const float *delta, const float *norm_w, float eps,
+                               float *h_out, float *y, int64_t hidden, int64_t inter, int act,
+                               void *ws, size_t ws_bytes, void *stream)
+{
+    if (!cols_ok(hidden) || !cols_ok(inter)) return Q4K_ERR_SHAPE;
+    if (act != Q4K_ACT_GELU_TANH && act != Q4K_ACT_SILU) return Q4K_ERR_ACT;
+    if (!Wg || !Wu || !Wd || !y) return Q4K_ERR_NULL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(y, 4))
+        return Q4K_ERR_ALIGN;
+    const size_t need = q4k_ffn_workspace_bytes(hidden, inter);
+    if (!ws || ws_bytes < need) return Q4K_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return Q4K_ERR_ALIGN;
+    const Span ins[3] = {span(Wg, wbytes(inter, hidden)), span(Wu, wbytes(inter, hidden)),
+                         span(Wd, wbytes(hidden, inter))};
+    const Span outs[2] = {span(y, hidden * 4), span(ws, (int64_t)need)};
+    if (overlap(outs[0], outs[1])) return Q4K_ERR_ALIAS;
+    for (int j = 0; j < 3; ++j)
+        if (overlap(outs[0], ins[j]) || overlap(outs[1], ins[j])) return Q4K_ERR_ALIAS;
+    const int c = norm_checks(h, delta, norm_w, eps, h_out, hidden, ins, 3, outs, 2);
+    if (c != Q4K_OK) return c;
+    const q4k::NormIn n = {delta, norm_w, eps, h_out};
+    return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                      (const uint8_t *)Wd, h, y, hidden, inter, act,
+                                      (float *)ws, as_stream(stream), &n));
 }
 
 // lm_head workspace: the per-workgroup candidate lists (k keys of 8 bytes

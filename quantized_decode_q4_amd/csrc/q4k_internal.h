@@ -19,17 +19,29 @@ constexpr int kMergeListsMax = 1024;    // per-workgroup candidate lists the mer
 // n/32 sums (f32).
 __host__ __device__ constexpr int64_t planes_bytes(int64_t n) { return 3 * n + n / 4; }
 
+// Residual RMSNorm fused into a projection's input: the activations become
+// s * w with s = x + delta (delta may be null) and the outputs are scaled by
+// 1/sqrt(mean(s^2) + eps); h_out (may be null) receives s.
+struct NormIn {
+    const float *delta;
+    const float *w;
+    float eps;
+    float *h_out;
+};
+
 // Row-streaming kernels (q4k_rows.hip).
 // y rows [0, split0) -> o0, [split0, split1) -> o1, [split1, rows) -> o2.
 hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float *o1, float *o2,
                              int64_t rows, int64_t cols, int64_t split0, int64_t split1,
-                             hipStream_t s);
+                             hipStream_t s, const NormIn *norm = nullptr);
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
-                          int64_t rows, int64_t cols, int act, hipStream_t s);
+                          int64_t rows, int64_t cols, int act, hipStream_t s,
+                          const NormIn *norm = nullptr);
 // Gated FFN: gate+up with the activation applied (h, f32[inter]), then the
-// down projection reading h.
+// down projection reading h. A norm applies to the gate+up input.
 hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
-                      float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s);
+                      float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s,
+                      const NormIn *norm = nullptr);
 // Q6_K matvec (GGUF Q6_K rows, 210 bytes per 256 weights): y = W x.
 hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t rows,
                              int64_t cols, hipStream_t s);

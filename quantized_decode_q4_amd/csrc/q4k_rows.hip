@@ -111,6 +111,9 @@ enum XSrc { XS_LDS = 0, XS_THREAD = 1, XS_F32 = 3 };
 // Weight format of the rows.
 enum Fmt { FMT_Q4K = 0, FMT_Q6K = 1 };
 constexpr int kQ6Bytes = 210;   // bytes per Q6_K super-block
+// Rows up to this many columns stage the normalised activations in LDS when a
+// norm is fused into an f32-activation launch (cols * 4 bytes).
+constexpr int64_t kNormLdsCols = 8192;
 
 __host__ __device__ constexpr int fmt_block_bytes(int fmt) { return fmt == FMT_Q6K ? kQ6Bytes : kBlockBytes; }
 
@@ -123,6 +126,13 @@ struct RowsArgs {
     float *o2;
     uint64_t *cand;          // EPI_LOGITS
     float2 *stats;           // EPI_LOGITS, optional: per-workgroup (max, sum of exp(l - max))
+    // Fused residual RMSNorm of the input (nw != nullptr): s = x + delta (delta
+    // optional), activations s * nw, every output scaled by
+    // 1/sqrt(mean(s^2) + eps); workgroup 0 writes s to h_out (optional).
+    const float *delta;
+    const float *nw;
+    float *h_out;
+    float eps;
     int64_t rows;
     int64_t split0;
     int64_t split1;
@@ -603,6 +613,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     __shared__ uint8_t taken[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint64_t keys_scratch[2][EPI == EPI_LOGITS ? NW : 1];
     __shared__ float sum_scratch[EPI == EPI_LOGITS ? NW : 1];
+    __shared__ float norm_scratch[NW];
     extern __shared__ uint4 xlds_v[];   // XS_LDS: planes of x (planes_bytes(cols))
     uint8_t *const xlds = reinterpret_cast<uint8_t *>(xlds_v);
 
@@ -652,6 +663,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int ngroups = (int)(cols / 8);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(cols * 4));
     uint4 xv[XS == XS_LDS ? 2 : 16];
+    uint32_t xoff[XS == XS_LDS ? 1 : 16];
     if (XS == XS_LDS) {
         const uint32_t xo = t < ngroups ? (uint32_t)t * 32u : kOutOfRange;
         xv[0] = bload16(rx, xo);
@@ -662,12 +674,14 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             const uint32_t xo =
                 uact ? (uint32_t)(256 * b + 128 * (g >> 1) + 16 * (g & 1)) * 4u : kOutOfRange;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xo + 128u * (i / 4) + 16u * (i % 4));
+            for (int i = 0; i < 16; ++i) xoff[i] = xo + 128u * (i / 4) + 16u * (i % 4);
         } else {
             const uint32_t xo = uact ? (uint32_t)(64 * u) * 4u : kOutOfRange;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xo + 16u * i);
+            for (int i = 0; i < 16; ++i) xoff[i] = xo + 16u * i;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xoff[i]);
     }
 
     using SlotT = std::conditional_t<FMT == FMT_Q6K, Slot6<NMAT>, Slot<NMAT>>;
@@ -681,11 +695,69 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 #pragma unroll
     for (int j = 0; j < D; ++j) issue(buf[j], slot_off(s_begin + j));
 
+    // ---- fused RMSNorm ----
+    // s = x + delta (f32) over the whole row (every workgroup reads it from L2),
+    // its sum of squares, and the new residual stream (workgroup 0). With
+    // activations converted in LDS this rides on the conversion loop below;
+    // otherwise one cooperative pass does it here and, for rows that fit,
+    // also leaves z = s * nw in LDS, so that the thread's own 64 activations
+    // are read from there: one memory round trip either way.
+    const bool norm = a.nw != nullptr;
+    const bool z_lds = norm && XS == XS_F32 && cols <= kNormLdsCols;
+    float *const zl = reinterpret_cast<float *>(xlds);
+    float inv_rms = 1.f;
+    float ss_part = 0.f;
+    float4 *const o4 = (norm && blockIdx.x == 0) ? reinterpret_cast<float4 *>(a.h_out) : nullptr;
+    const __amdgpu_buffer_rsrc_t rdel = make_rsrc(a.delta, a.delta ? (uint32_t)(cols * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rnw = make_rsrc(a.nw, norm ? (uint32_t)(cols * 4) : 0u);
+    // s of four activations at byte offset off (x given), and z = s * nw
+    auto norm4 = [&](uint4 hv, uint32_t off, float4 &sv) -> uint4 {
+        const uint4 dv = bload16(rdel, off), wv = bload16(rnw, off);
+        sv = make_float4(__uint_as_float(hv.x), __uint_as_float(hv.y), __uint_as_float(hv.z),
+                         __uint_as_float(hv.w));
+        if (a.delta) {
+            sv.x += __uint_as_float(dv.x); sv.y += __uint_as_float(dv.y);
+            sv.z += __uint_as_float(dv.z); sv.w += __uint_as_float(dv.w);
+        }
+        return make_uint4(__float_as_uint(sv.x * __uint_as_float(wv.x)),
+                          __float_as_uint(sv.y * __uint_as_float(wv.y)),
+                          __float_as_uint(sv.z * __uint_as_float(wv.z)),
+                          __float_as_uint(sv.w * __uint_as_float(wv.w)));
+    };
+    auto add_sq = [&](const float4 &v) {
+        ss_part = fmaf(v.x, v.x, ss_part);
+        ss_part = fmaf(v.y, v.y, ss_part);
+        ss_part = fmaf(v.z, v.z, ss_part);
+        ss_part = fmaf(v.w, v.w, ss_part);
+    };
+    if (norm && XS != XS_LDS) {
+        const int n4 = (int)(cols / 4);
+        for (int i = t; i < n4; i += blockDim.x) {
+            const uint32_t off = (uint32_t)i * 16u;
+            float4 sv;
+            const uint4 z = norm4(bload16(rx, off), off, sv);
+            add_sq(sv);
+            if (o4) o4[i] = sv;
+            if (z_lds) *reinterpret_cast<uint4 *>(zl + 4 * i) = z;
+        }
+        const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes zl
+        inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
+    }
+
     // ---- the thread's activations (unused units: zeros) ----
     XUnit xu;
     XF32 xf;
     float s6[4] = {0.f, 0.f, 0.f, 0.f};   // Q6_K: sums of the four quarters
     if (XS == XS_THREAD || XS == XS_F32) {
+        if (z_lds) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                xv[i] = uact ? *reinterpret_cast<const uint4 *>(xlds + xoff[i]) : make_uint4(0, 0, 0, 0);
+        } else if (norm) {
+            float4 sv;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xv[i] = norm4(xv[i], xoff[i], sv);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             xf.xa[4 * i + 0] = __uint_as_float(xv[i].x); xf.xa[4 * i + 1] = __uint_as_float(xv[i].y);
@@ -720,10 +792,21 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         float *Ss = Xs + cols / 32;
         for (int e0 = 0; e0 < ngroups; e0 += blockDim.x) {
             const int e = e0 + t;   // uniform trip count; blockDim % 4 == 0
+            const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
             if (e0 > 0) {
-                const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
                 xv[0] = bload16(rx, xo);
                 xv[1] = bload16(rx, xo + 16u);
+            }
+            if (norm) {
+                float4 s0, s1;
+                xv[0] = norm4(xv[0], xo, s0);
+                xv[1] = norm4(xv[1], xo + 16u, s1);
+                add_sq(s0);
+                add_sq(s1);
+                if (o4 && e < ngroups) {
+                    o4[2 * e] = s0;
+                    o4[2 * e + 1] = s1;
+                }
             }
             const float v[8] = {__uint_as_float(xv[0].x), __uint_as_float(xv[0].y),
                                 __uint_as_float(xv[0].z), __uint_as_float(xv[0].w),
@@ -760,7 +843,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 }
             }
         }
-        __syncthreads();
+        if (norm) {
+            const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes the planes
+            inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
+        } else {
+            __syncthreads();
+        }
         // This unit's planes: 64 bytes per plane at 64u, X and S at 2u.
         if (uact) {
 #pragma unroll
@@ -811,6 +899,10 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                     for (int w = 0; w < nwaves; ++w) {
                         v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
                         if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
+                    }
+                    if (norm) {
+                        v0 *= inv_rms;
+                        v1 *= inv_rms;
                     }
                     if (EPI == EPI_STORE) {
                         if (row < a.split0)
@@ -1044,7 +1136,9 @@ hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hip
 {
     const dim3 grid((unsigned)nwg), block((unsigned)threads);
     const int64_t cols = (int64_t)a.nb * kQK;
-    const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols) : 0;
+    const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols)
+                       : (a.nw && XS == XS_F32 && cols <= kNormLdsCols) ? (size_t)(cols * 4)
+                                                                         : 0;
     if (threads > 512) {
         // only reachable with one row per sweep (cols > 32768: no LDS planes)
         hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, XS == XS_LDS ? XS_THREAD : XS, 1024, 0, FMT>),
@@ -1110,11 +1204,21 @@ constexpr int kLmheadWgsMax = 1024;  // bounds the candidate workspace
 
 }  // namespace
 
+void set_norm(RowsArgs &a, const NormIn *norm)
+{
+    if (!norm) return;
+    a.delta = norm->delta;
+    a.nw = norm->w;
+    a.eps = norm->eps;
+    a.h_out = norm->h_out;
+}
+
 hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float *o1, float *o2,
                              int64_t rows, int64_t cols, int64_t split0, int64_t split1,
-                             hipStream_t s)
+                             hipStream_t s, const NormIn *norm)
 {
     RowsArgs a = base_args(rows, cols);
+    set_norm(a, norm);
     a.W0 = W;
     a.x = x;
     a.o0 = o0;
@@ -1134,9 +1238,10 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
 }
 
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
-                          int64_t rows, int64_t cols, int act, hipStream_t s)
+                          int64_t rows, int64_t cols, int act, hipStream_t s, const NormIn *norm)
 {
     RowsArgs a = base_args(rows, cols);
+    set_norm(a, norm);
     a.W0 = Wg;
     a.W1 = Wu;
     a.x = x;
@@ -1148,9 +1253,10 @@ hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, 
 }
 
 hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
-                      float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s)
+                      float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s,
+                      const NormIn *norm)
 {
-    hipError_t e = launch_gate_up(Wg, Wu, x, h, inter, hidden, act, s);
+    hipError_t e = launch_gate_up(Wg, Wu, x, h, inter, hidden, act, s, norm);
     if (e != hipSuccess) return e;
     // down projection: few rows per thread, so f32 activations (no conversion)
     RowsArgs b = base_args(hidden, inter);

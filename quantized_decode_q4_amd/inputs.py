@@ -29,7 +29,8 @@ rounded to binary16.
 
 Seeding: numpy PCG64 via ``default_rng([0x51344B, config, tensor_id, index])``.
 Configs: 0 tiny matvec, 1 QKV, 2 FFN, 3 lm_head, 4 prefill activations, 5 the
-attention output projection, 6 Q6_K matvec at the down-projection shape.
+attention output projection, 6 Q6_K matvec at the down-projection shape, 7 the
+residual stream and norm weights of the fused RMSNorm.
 Tensor ids: 0 = W / Wqkv / Wg, 1 = Wu, 2 = Wd, 3 = x / X. ``index`` is the layer
 or copy number. Draw order inside ``q4k_random``: the 144-byte rows of raw bytes
 first, then all d values, then all dmin values (row-major over blocks).
@@ -141,6 +142,15 @@ def q6k_down(layer: int = 0, hidden: int = HIDDEN, inter: int = INTER):
     """Q6_K matvec at the FFN down-projection shape: W hidden x inter, x ~ N(0,1)."""
     return {"W": q6k_random(rng_for(6, 0, layer), hidden, inter),
             "x": normal_f32(rng_for(6, 3, layer), inter)}
+
+
+def norm_inputs(index: int = 0, n: int = HIDDEN):
+    """Residual RMSNorm inputs: stream h ~ 4 N(0,1), delta ~ N(0,1), norm weight
+    w = 1 + 0.1 N(0,1) (all f32), eps = 1e-6."""
+    return {"h": normal_f32(rng_for(7, 0, index), n, scale=4.0),
+            "delta": normal_f32(rng_for(7, 1, index), n),
+            "w": (1.0 + 0.1 * rng_for(7, 2, index).standard_normal(n)).astype(np.float32),
+            "eps": 1e-6}
 
 
 def prefill_x(seq: int = PREFILL_SEQ, hidden: int = HIDDEN, index: int = 0):

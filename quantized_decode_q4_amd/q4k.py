@@ -24,6 +24,7 @@ Q4K_ERR_ACT = -5
 Q4K_ERR_WORKSPACE = -6
 Q4K_ERR_ALIAS = -7
 Q4K_ERR_HIP = -8
+Q4K_ERR_EPS = -9
 Q4K_ACT_GELU_TANH = 0
 Q4K_ACT_SILU = 1
 Q4K_TOPK_MAX = 64
@@ -42,6 +43,7 @@ if not os.path.exists(LIB_PATH):
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
 _INT = ctypes.c_int
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -54,6 +56,9 @@ _SIGS = {
     "q4k_lmhead_workspace_bytes": ([_I64, _I64, _INT], _SZ),
     "q4k_lmhead_topk": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _SZ, _P], _INT),
     "q6k_matvec": ([_P, _P, _P, _I64, _I64, _P], _INT),
+    "q4k_rmsnorm_matvec": ([_P, _P, _P, _P, _F32, _P, _P, _I64, _I64, _P], _INT),
+    "q4k_rmsnorm_ffn": ([_P, _P, _P, _P, _P, _P, _F32, _P, _P, _I64, _I64, _INT, _P, _SZ, _P],
+                        _INT),
     "q4k_lmhead_topk_probs": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P, _P, _SZ, _P], _INT),
     "q4k_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4k_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
@@ -109,6 +114,22 @@ def q4k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
 
 def q6k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
     _check(lib.q6k_matvec(_ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)), "q6k_matvec")
+
+
+def q4k_rmsnorm_matvec(W, h, delta, norm_w, eps: float, h_out, y, rows: int, cols: int,
+                       stream=None) -> None:
+    _check(lib.q4k_rmsnorm_matvec(_ptr(W), _ptr(h), _ptr(delta), _ptr(norm_w), float(eps),
+                                  _ptr(h_out), _ptr(y), rows, cols, _stream(stream)),
+           "q4k_rmsnorm_matvec")
+
+
+def q4k_rmsnorm_ffn(Wg, Wu, Wd, h, delta, norm_w, eps: float, h_out, y, hidden: int, inter: int,
+                    act: int, ws, ws_bytes: int | None = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = _nbytes(ws)
+    _check(lib.q4k_rmsnorm_ffn(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(h), _ptr(delta), _ptr(norm_w),
+                               float(eps), _ptr(h_out), _ptr(y), hidden, inter, act, _ptr(ws),
+                               ws_bytes, _stream(stream)), "q4k_rmsnorm_ffn")
 
 
 def q4k_qkv(Wqkv, x, q, k, v, q_rows: int, kv_rows: int, cols: int, stream=None) -> None:

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["q4k_matvec", "q4k_qkv", "q4k_ffn", "q4k_gate_up", "q4k_lmhead_topk",
-              "q4k_lmhead_topk_probs", "q4k_matmul",
+              "q4k_lmhead_topk_probs", "q6k_matvec", "q4k_rmsnorm_matvec", "q4k_rmsnorm_ffn",
+              "q4k_matmul",
               "q4k_ffn_prefill", "q4k_status_string", "q4k_last_hip_error",
               "q4k_ffn_workspace_bytes", "q4k_lmhead_workspace_bytes",
               "q4k_matmul_workspace_bytes", "q4k_ffn_prefill_workspace_bytes"]:
@@ -49,7 +50,7 @@ def test_library_exports_nothing_else():
 
 
 def test_status_strings():
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert q4k.q4k_status_string(s)
     assert "unknown" in q4k.q4k_status_string(-99)
     assert q4k.q4k_last_hip_error() == ""
@@ -117,6 +118,38 @@ def test_q6k_matvec_validation():
     assert P(A, B, A + 2096, 10, 256, S) == q4k.Q4K_ERR_ALIAS   # y inside W (10 x 210 B)
     assert P(A, B, B + 512, 10, 256, S) == q4k.Q4K_ERR_ALIAS    # y inside x
     assert P(None, None, None, 0, 256, S) == q4k.Q4K_OK         # rows = 0: nothing to do
+
+
+def test_rmsnorm_validation():
+    G = 0x7F6000000000
+    H = 0x7F7000000000
+    M = L.q4k_rmsnorm_matvec
+    # W, h, delta, w, eps, h_out, y, rows, cols
+    assert M(A, B, C, D, 1e-6, E, F, 0, 256, S) == q4k.Q4K_ERR_SHAPE
+    assert M(A, B, C, D, 1e-6, E, F, 10, 100, S) == q4k.Q4K_ERR_SHAPE
+    assert M(A, None, C, D, 1e-6, E, F, 10, 256, S) == q4k.Q4K_ERR_NULL
+    assert M(A, B, C, None, 1e-6, E, F, 10, 256, S) == q4k.Q4K_ERR_NULL
+    assert M(A, B, C, D, -1.0, E, F, 10, 256, S) == q4k.Q4K_ERR_EPS
+    assert M(A, B, C, D, float("nan"), E, F, 10, 256, S) == q4k.Q4K_ERR_EPS
+    assert M(A, B, C, D, float("inf"), E, F, 10, 256, S) == q4k.Q4K_ERR_EPS
+    assert M(A, B + 4, C, D, 1e-6, E, F, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert M(A, B, C + 8, D, 1e-6, E, F, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert M(A, B, C, D, 1e-6, E + 4, F, 10, 256, S) == q4k.Q4K_ERR_ALIGN
+    assert M(A, B, C, D, 1e-6, B, F, 10, 256, S) == q4k.Q4K_ERR_ALIAS        # h_out on h
+    assert M(A, B, C, D, 1e-6, C + 512, F, 10, 256, S) == q4k.Q4K_ERR_ALIAS  # h_out in delta
+    assert M(A, B, C, D, 1e-6, A + 32, F, 10, 256, S) == q4k.Q4K_ERR_ALIAS   # h_out in W
+    assert M(A, B, C, D, 1e-6, F + 16, F, 10, 256, S) == q4k.Q4K_ERR_ALIAS   # h_out on y
+    assert M(A, B, C, D, 1e-6, E, D + 4, 10, 256, S) == q4k.Q4K_ERR_ALIAS    # y in norm_w
+    assert M(A, B, C, D, 1e-6, E, A + 8, 10, 256, S) == q4k.Q4K_ERR_ALIAS    # y in W
+    Fn = L.q4k_rmsnorm_ffn
+    need = q4k.q4k_ffn_workspace_bytes(256, 512)
+    # Wg, Wu, Wd, h, delta, w, eps, h_out, y, hidden, inter, act, ws, ws_bytes
+    assert Fn(A, B, C, D, None, E, 1e-6, None, F, 256, 512, 7, G, need, S) == q4k.Q4K_ERR_ACT
+    assert Fn(A, B, C, D, None, E, -2.0, None, F, 256, 512, 0, G, need, S) == q4k.Q4K_ERR_EPS
+    assert Fn(A, B, C, D, None, E, 1e-6, None, F, 256, 512, 0, G, need - 4, S) == q4k.Q4K_ERR_WORKSPACE
+    assert Fn(A, B, C, None, None, E, 1e-6, None, F, 256, 512, 0, G, need, S) == q4k.Q4K_ERR_NULL
+    assert Fn(A, B, C, D, None, E, 1e-6, G + 64, F, 256, 512, 0, G, need, S) == q4k.Q4K_ERR_ALIAS  # h_out in ws
+    assert Fn(A, B, C, D, None, E, 1e-6, H, D + 16, 256, 512, 0, G, need, S) == q4k.Q4K_ERR_ALIAS  # y on h
 
 
 def test_lmhead_validation():
