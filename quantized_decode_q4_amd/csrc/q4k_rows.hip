@@ -82,6 +82,9 @@
 #ifndef Q4K_DOWN_WGS_PER_CU
 #define Q4K_DOWN_WGS_PER_CU 1
 #endif
+#ifndef Q4K_PRE_SWEEPS
+#define Q4K_PRE_SWEEPS 1            // sweeps issued before the activations are prepared
+#endif
 #ifndef Q6K_D
 #define Q6K_D 1                     // sweeps in flight, Q6_K matvec
 #endif
@@ -660,14 +663,28 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // ---- activation loads go out first, then the first D sweeps ----
     // XS_LDS: this thread's first group of 8 activations (the first pass of
     // the cooperative conversion); XS_THREAD / XS_F32: the unit's 64 floats.
+    // With a fused norm, its inputs for the first group (XS_LDS) or the first
+    // two steps of the norm pass (XS_F32 staging through LDS) go out here too.
     const int ngroups = (int)(cols / 8);
+    const int n4 = (int)(cols / 4);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(cols * 4));
+    const bool norm = a.nw != nullptr;
+    const bool z_lds = norm && XS == XS_F32 && cols <= kNormLdsCols;
+    const __amdgpu_buffer_rsrc_t rdel = make_rsrc(a.delta, a.delta ? (uint32_t)(cols * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rnw = make_rsrc(a.nw, norm ? (uint32_t)(cols * 4) : 0u);
     uint4 xv[XS == XS_LDS ? 2 : 16];
     uint32_t xoff[XS == XS_LDS ? 1 : 16];
+    uint4 nv[XS == XS_LDS ? 4 : 6];   // norm inputs issued with x (see above)
     if (XS == XS_LDS) {
         const uint32_t xo = t < ngroups ? (uint32_t)t * 32u : kOutOfRange;
         xv[0] = bload16(rx, xo);
         xv[1] = bload16(rx, xo + 16u);
+        if (norm) {
+            nv[0] = bload16(rdel, xo);
+            nv[1] = bload16(rdel, xo + 16u);
+            nv[2] = bload16(rnw, xo);
+            nv[3] = bload16(rnw, xo + 16u);
+        }
     } else {
         if (FMT == FMT_Q6K) {
             // quarters j = 0..3 of unit (b, n, h): x[256b + 128n + 32j + 16h + i]
@@ -680,9 +697,24 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) xoff[i] = xo + 16u * i;
         }
+        if (z_lds) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xoff[i]);
+            for (int k = 0; k < 2; ++k) {
+                const int i = t + k * (int)blockDim.x;
+                const uint32_t off = i < n4 ? (uint32_t)i * 16u : kOutOfRange;
+                nv[3 * k] = bload16(rx, off);
+                nv[3 * k + 1] = bload16(rdel, off);
+                nv[3 * k + 2] = bload16(rnw, off);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xv[i] = bload16(rx, xoff[i]);
+        }
     }
+    // The activation loads must leave before the weight loads: the wait
+    // counter is in order, so waiting for x would otherwise also wait for the
+    // first sweeps of weights. A compiler barrier keeps that order.
+    asm volatile("" ::: "memory");
 
     using SlotT = std::conditional_t<FMT == FMT_Q6K, Slot6<NMAT>, Slot<NMAT>>;
     auto issue = [&](SlotT &sl, uint32_t off) {
@@ -691,9 +723,13 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         else
             load_slot<NMAT>(sl, rs, off, qoff);
     };
+    // The first kPre sweeps go out before the activations are prepared, the
+    // rest of the first D right after (a deeper early burst delays the
+    // activation reads, which every sweep waits for).
+    constexpr int kPre = D < Q4K_PRE_SWEEPS ? D : Q4K_PRE_SWEEPS;
     SlotT buf[D + 1];
 #pragma unroll
-    for (int j = 0; j < D; ++j) issue(buf[j], slot_off(s_begin + j));
+    for (int j = 0; j < kPre; ++j) issue(buf[j], slot_off(s_begin + j));
 
     // ---- fused RMSNorm ----
     // s = x + delta (f32) over the whole row (every workgroup reads it from L2),
@@ -702,17 +738,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // otherwise one cooperative pass does it here and, for rows that fit,
     // also leaves z = s * nw in LDS, so that the thread's own 64 activations
     // are read from there: one memory round trip either way.
-    const bool norm = a.nw != nullptr;
-    const bool z_lds = norm && XS == XS_F32 && cols <= kNormLdsCols;
     float *const zl = reinterpret_cast<float *>(xlds);
     float inv_rms = 1.f;
     float ss_part = 0.f;
     float4 *const o4 = (norm && blockIdx.x == 0) ? reinterpret_cast<float4 *>(a.h_out) : nullptr;
-    const __amdgpu_buffer_rsrc_t rdel = make_rsrc(a.delta, a.delta ? (uint32_t)(cols * 4) : 0u);
-    const __amdgpu_buffer_rsrc_t rnw = make_rsrc(a.nw, norm ? (uint32_t)(cols * 4) : 0u);
-    // s of four activations at byte offset off (x given), and z = s * nw
-    auto norm4 = [&](uint4 hv, uint32_t off, float4 &sv) -> uint4 {
-        const uint4 dv = bload16(rdel, off), wv = bload16(rnw, off);
+    // s of four activations (x, delta and nw given), and z = s * nw
+    auto norm4 = [&](uint4 hv, uint4 dv, uint4 wv, float4 &sv) -> uint4 {
         sv = make_float4(__uint_as_float(hv.x), __uint_as_float(hv.y), __uint_as_float(hv.z),
                          __uint_as_float(hv.w));
         if (a.delta) {
@@ -731,14 +762,22 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         ss_part = fmaf(v.w, v.w, ss_part);
     };
     if (norm && XS != XS_LDS) {
-        const int n4 = (int)(cols / 4);
-        for (int i = t; i < n4; i += blockDim.x) {
-            const uint32_t off = (uint32_t)i * 16u;
+        auto pass_step = [&](int i, uint4 hv, uint4 dv, uint4 wv) {
             float4 sv;
-            const uint4 z = norm4(bload16(rx, off), off, sv);
+            const uint4 z = norm4(hv, dv, wv, sv);
             add_sq(sv);
             if (o4) o4[i] = sv;
             if (z_lds) *reinterpret_cast<uint4 *>(zl + 4 * i) = z;
+        };
+        int i0 = t;
+        if (z_lds) {   // the first two steps were loaded with x
+            if (t < n4) pass_step(t, nv[0], nv[1], nv[2]);
+            if (t + (int)blockDim.x < n4) pass_step(t + blockDim.x, nv[3], nv[4], nv[5]);
+            i0 = t + 2 * (int)blockDim.x;
+        }
+        for (int i = i0; i < n4; i += blockDim.x) {
+            const uint32_t off = (uint32_t)i * 16u;
+            pass_step(i, bload16(rx, off), bload16(rdel, off), bload16(rnw, off));
         }
         const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes zl
         inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
@@ -756,7 +795,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         } else if (norm) {
             float4 sv;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xv[i] = norm4(xv[i], xoff[i], sv);
+            for (int i = 0; i < 16; ++i)
+                xv[i] = norm4(xv[i], bload16(rdel, xoff[i]), bload16(rnw, xoff[i]), sv);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -790,17 +830,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         // activations each; max and sum over the 4 lanes by xor shuffles.
         float *Xs = reinterpret_cast<float *>(xlds + 3 * cols);
         float *Ss = Xs + cols / 32;
-        for (int e0 = 0; e0 < ngroups; e0 += blockDim.x) {
-            const int e = e0 + t;   // uniform trip count; blockDim % 4 == 0
-            const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
-            if (e0 > 0) {
-                xv[0] = bload16(rx, xo);
-                xv[1] = bload16(rx, xo + 16u);
-            }
+        // group e of 8 activations (x, and with a norm delta and nw, given)
+        auto convert = [&](int e, uint4 h0, uint4 h1, uint4 d0, uint4 d1, uint4 w0, uint4 w1) {
             if (norm) {
                 float4 s0, s1;
-                xv[0] = norm4(xv[0], xo, s0);
-                xv[1] = norm4(xv[1], xo + 16u, s1);
+                h0 = norm4(h0, d0, w0, s0);
+                h1 = norm4(h1, d1, w1, s1);
                 add_sq(s0);
                 add_sq(s1);
                 if (o4 && e < ngroups) {
@@ -808,10 +843,10 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                     o4[2 * e + 1] = s1;
                 }
             }
-            const float v[8] = {__uint_as_float(xv[0].x), __uint_as_float(xv[0].y),
-                                __uint_as_float(xv[0].z), __uint_as_float(xv[0].w),
-                                __uint_as_float(xv[1].x), __uint_as_float(xv[1].y),
-                                __uint_as_float(xv[1].z), __uint_as_float(xv[1].w)};
+            const float v[8] = {__uint_as_float(h0.x), __uint_as_float(h0.y),
+                                __uint_as_float(h0.z), __uint_as_float(h0.w),
+                                __uint_as_float(h1.x), __uint_as_float(h1.y),
+                                __uint_as_float(h1.z), __uint_as_float(h1.w)};
             float amax = 0.f, sum = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -842,6 +877,25 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                     Ss[e >> 2] = sum;
                 }
             }
+        };
+        // The first group was loaded before the weights; later ones (rows
+        // wider than 8 * blockDim) are loaded here. Trip counts are uniform
+        // (blockDim % 4 == 0), so the xor shuffles see whole quads.
+        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+        convert(t, xv[0], xv[1], norm ? nv[0] : zero4, norm ? nv[1] : zero4,
+                norm ? nv[2] : zero4, norm ? nv[3] : zero4);
+        for (int e0 = blockDim.x; e0 < ngroups; e0 += blockDim.x) {
+            const int e = e0 + t;
+            const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
+            const uint4 h0 = bload16(rx, xo), h1 = bload16(rx, xo + 16u);
+            uint4 d0 = zero4, d1 = zero4, w0 = zero4, w1 = zero4;
+            if (norm) {
+                d0 = bload16(rdel, xo);
+                d1 = bload16(rdel, xo + 16u);
+                w0 = bload16(rnw, xo);
+                w1 = bload16(rnw, xo + 16u);
+            }
+            convert(e, h0, h1, d0, d1, w0, w1);
         }
         if (norm) {
             const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes the planes
@@ -875,6 +929,9 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 
     // One sweep: dot products, wave reduction, and every fb sweeps the
     // cross-wave reduction and epilogue of that batch of rows.
+#pragma unroll
+    for (int j = kPre; j < D; ++j) issue(buf[j], slot_off(s_begin + j));
+
     int kb = 0, bank = 0;
     auto compute_sweep = [&](const SlotT &sl, int64_t sj) {
 #pragma unroll
