@@ -85,6 +85,9 @@
 #ifndef Q4K_PRE_SWEEPS
 #define Q4K_PRE_SWEEPS 1            // sweeps issued before the activations are prepared
 #endif
+#ifndef Q4K_INTERLEAVE
+#define Q4K_INTERLEAVE 1            // long launches: workgroups take every G-th sweep
+#endif
 #ifndef Q6K_D
 #define Q6K_D 1                     // sweeps in flight, Q6_K matvec
 #endif
@@ -117,6 +120,8 @@ constexpr int kQ6Bytes = 210;   // bytes per Q6_K super-block
 // Rows up to this many columns stage the normalised activations in LDS when a
 // norm is fused into an f32-activation launch (cols * 4 bytes).
 constexpr int64_t kNormLdsCols = 8192;
+// Sweeps per workgroup from which a launch interleaves its sweeps.
+constexpr int64_t kIlvMinSweeps = 8;
 
 __host__ __device__ constexpr int fmt_block_bytes(int fmt) { return fmt == FMT_Q6K ? kQ6Bytes : kBlockBytes; }
 
@@ -144,6 +149,7 @@ struct RowsArgs {
     int32_t act;
     int32_t k;
     int32_t chunk;           // sweeps per unit of the workgroup split
+    int32_t ilv;             // 1: workgroup w takes sweeps w, w+G, w+2G, ... (else a contiguous range)
 };
 
 __device__ __forceinline__ float act_apply(float z, int act)
@@ -635,10 +641,18 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int64_t rowbytes = (int64_t)a.nb * fmt_block_bytes(FMT);
     const int64_t unit_off = (int64_t)b * fmt_block_bytes(FMT);
     const int64_t S = (a.rows + RPS - 1) / RPS;
-    const int64_t s_begin = S * blockIdx.x / gridDim.x;
-    const int64_t s_end = S * (blockIdx.x + 1) / gridDim.x;
-    const int64_t row_begin = s_begin * RPS;
-    const int64_t row_stop = min(s_end * RPS, a.rows);
+    // The workgroup's sweeps, by local index i = 0 .. n_loc-1: either the
+    // contiguous range [s_begin, s_end), or (ilv) sweeps w, w+G, w+2G, ... so
+    // that all workgroups move through the matrix together.
+    const bool ilv = a.ilv != 0;
+    const int64_t G = gridDim.x, wg = blockIdx.x;
+    const int64_t s_begin = ilv ? wg : S * wg / G;
+    const int64_t n_loc = ilv ? (S > wg ? (S - wg + G - 1) / G : 0) : S * (wg + 1) / G - s_begin;
+    const int64_t s_step = ilv ? G : 1;
+    auto gsweep = [&](int64_t i) -> int64_t { return s_begin + i * s_step; };
+    // first row the resource starts at; rows of this workgroup: [row_begin, row_span_end)
+    const int64_t row_begin = ilv ? 0 : s_begin * RPS;
+    const int64_t row_span_end = ilv ? a.rows : min((s_begin + n_loc) * RPS, a.rows);
 
     // Buffer resources over this workgroup's rows (the host keeps the span
     // below 2^30 bytes); offsets are relative to row_begin. Q6_K rows start at
@@ -650,12 +664,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     for (int m = 0; m < NMAT; ++m) {
         const uint8_t *base = (m == 0 ? a.W0 : a.W1) + row_begin * rowbytes;
         if (FMT == FMT_Q6K) lead = (uint32_t)((uintptr_t)base & 3u);
-        rs[m] = make_rsrc(base - lead, (uint32_t)((row_stop - row_begin) * rowbytes) + lead);
+        rs[m] = make_rsrc(base - lead, (uint32_t)((row_span_end - row_begin) * rowbytes) + lead);
     }
     const uint32_t qoff = 16u + 32u * (uint32_t)g;
-    auto slot_off = [&](int64_t sw) -> uint32_t {
-        const int64_t row = sw * RPS + r;
-        return (uact && row < row_stop)
+    auto slot_off = [&](int64_t i) -> uint32_t {
+        const int64_t row = gsweep(i) * RPS + r;
+        return (uact && i < n_loc && row < a.rows)
                    ? (uint32_t)((row - row_begin) * rowbytes + unit_off) + lead
                    : kOutOfRange;
     };
@@ -729,7 +743,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     constexpr int kPre = D < Q4K_PRE_SWEEPS ? D : Q4K_PRE_SWEEPS;
     SlotT buf[D + 1];
 #pragma unroll
-    for (int j = 0; j < kPre; ++j) issue(buf[j], slot_off(s_begin + j));
+    for (int j = 0; j < kPre; ++j) issue(buf[j], slot_off(j));
 
     // ---- fused RMSNorm ----
     // s = x + delta (f32) over the whole row (every workgroup reads it from L2),
@@ -930,7 +944,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // One sweep: dot products, wave reduction, and every fb sweeps the
     // cross-wave reduction and epilogue of that batch of rows.
 #pragma unroll
-    for (int j = kPre; j < D; ++j) issue(buf[j], slot_off(s_begin + j));
+    for (int j = kPre; j < D; ++j) issue(buf[j], slot_off(j));
 
     int kb = 0, bank = 0;
     auto compute_sweep = [&](const SlotT &sl, int64_t sj) {
@@ -946,12 +960,13 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             if (lane < RPS) red[bank][wave][(kb * NMAT + m) * RPS + lane] = v;
         }
         ++kb;
-        if (kb == fb || sj == s_end - 1) {
+        if (kb == fb || sj == n_loc - 1) {
             __syncthreads();
             if (t < kb * RPS) {
                 const int k = t / RPS, rr = t % RPS;
-                const int64_t row = (sj - kb + 1) * RPS + t;
-                if (row < row_stop) {
+                const int64_t li = sj - kb + 1 + k;         // local sweep of this row
+                const int64_t row = gsweep(li) * RPS + rr;
+                if (row < a.rows) {
                     float v0 = 0.f, v1 = 0.f;
                     for (int w = 0; w < nwaves; ++w) {
                         v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
@@ -972,8 +987,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                         a.o0[row] = act_apply(v0, a.act) * v1;
                     } else {
                         a.o0[row] = v0;
-                        lg[row - row_begin] = v0;
-                        taken[row - row_begin] = 0;
+                        lg[li * RPS + rr] = v0;
+                        taken[li * RPS + rr] = 0;
                     }
                 }
             }
@@ -986,8 +1001,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // by step j-1 and computes sweep s+j. No early exit inside a group keeps
     // the ring's wait counts exact (only the oldest sweep is waited for).
     // Prefetches past the workgroup's last sweep read zeros.
-    int64_t s = s_begin;
-    for (; s + D < s_end; s += D + 1) {
+    int64_t s = 0;
+    for (; s + D < n_loc; s += D + 1) {
 #pragma unroll
         for (int j = 0; j <= D; ++j) {
             if (D > 0) issue(buf[(j + D) % (D + 1)], slot_off(s + j + D));
@@ -998,7 +1013,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // Tail: fewer than D+1 sweeps left, all already in flight in buf[0..].
 #pragma unroll
     for (int j = 0; j < (D > 0 ? D : 1); ++j) {
-        if (s + j < s_end) {
+        if (s + j < n_loc) {
             if (D == 0) issue(buf[0], slot_off(s + j));
             compute_sweep(buf[j], s + j);
         }
@@ -1010,20 +1025,25 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         // winning row (row j is scanned by thread j mod blockDim) marks it
         // taken, so the mark needs no barrier of its own.
         __syncthreads();
-        const int n = (int)(row_stop - row_begin);
+        // local row j = i * RPS + rr is global row gsweep(i) * RPS + rr; rows
+        // past the end (a partial last sweep) are skipped
+        const int n = (int)(n_loc * RPS);
+        auto grow = [&](int j) -> int64_t { return gsweep(j / RPS) * RPS + j % RPS; };
         uint64_t *out = a.cand + (int64_t)blockIdx.x * a.k;
         float wg_max = 0.f;
         for (int round = 0; round < a.k; ++round) {
             uint64_t best = 0;
             for (int j = t; j < n; j += blockDim.x) {
-                if (taken[j]) continue;
-                const uint64_t kk = topk_key(lg[j], (uint32_t)(row_begin + j));
+                const int64_t gr = grow(j);
+                if (gr >= a.rows || taken[j]) continue;
+                const uint64_t kk = topk_key(lg[j], (uint32_t)gr);
                 best = kk > best ? kk : best;
             }
             const uint64_t win = block_max_u64(best, keys_scratch[round & 1]);
             if (round == 0) wg_max = topk_key_value(win);
             if (win != 0) {
-                const int j = (int)((int64_t)(~(uint32_t)(win & 0xFFFFFFFFu)) - row_begin);
+                const int64_t gr = (int64_t)(~(uint32_t)(win & 0xFFFFFFFFu));
+                const int j = (int)(((gr / RPS) - s_begin) / s_step * RPS + gr % RPS);
                 if (j % (int)blockDim.x == t) taken[j] = 1;
             }
             if (t == 0) out[round] = win;
@@ -1035,7 +1055,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             // rows add 0 and NaN rows poison the sum.
             const float base = wg_max == -INFINITY ? 0.f : wg_max;
             float sum = 0.f;
-            for (int j = t; j < n; j += blockDim.x) sum += expf(lg[j] - base);
+            for (int j = t; j < n; j += blockDim.x)
+                if (grow(j) < a.rows) sum += expf(lg[j] - base);
             sum = block_sum_f32(sum, sum_scratch);
             if (t == 0) a.stats[blockIdx.x] = make_float2(wg_max, sum);
         }
@@ -1189,8 +1210,18 @@ int device_cus()
 }
 
 template <int NMAT, int EPI, int XS, int D, int FMT = FMT_Q4K>
-hipError_t launch_rows(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s)
+hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hipStream_t s)
 {
+    // Long launches (at least kIlvMinSweeps sweeps per workgroup) interleave
+    // their sweeps across workgroups: lm_head 80.6 -> 78.3 us, while the
+    // 2-5-sweep decode launches measured flat or slightly slower. Interleaved
+    // sweeps need one buffer resource over the whole matrix (<= 1 GiB).
+    RowsArgs a = a0;
+    const int64_t sweeps = (a.rows + rps - 1) / rps;
+    a.ilv = (Q4K_INTERLEAVE && sweeps >= kIlvMinSweeps * nwg &&
+             a.rows * (int64_t)a.nb * fmt_block_bytes(FMT) <= ((int64_t)1 << 30))
+                ? 1
+                : 0;
     const dim3 grid((unsigned)nwg), block((unsigned)threads);
     const int64_t cols = (int64_t)a.nb * kQK;
     const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols)

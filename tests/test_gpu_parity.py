@@ -328,6 +328,52 @@ def test_lmhead_nan_rows_rank_last(q4k, orc):
     assert ti.tolist() == ridx.tolist()
 
 
+# ------------------------------------- long launches (interleaved sweeps) ---
+# Launches with at least 8 sweeps per workgroup hand out sweeps round-robin
+# (workgroup w takes w, w+G, ...). These shapes reach that mode with a
+# partial last sweep.
+
+def test_interleaved_matvec_and_gate_up(q4k, orc):
+    rng = np.random.default_rng(95)
+    rows, cols = 30001, 2560
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    y = gpu_matvec(q4k, W, x, rows, cols)
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(y, ref, A, what="matvec 30001x2560 (interleaved)")
+    inter, hidden = 20001, 2560
+    Wg = inputs.q4k_random(rng, inter, hidden)
+    Wu = inputs.q4k_random(rng, inter, hidden)
+    h = torch.full((inter,), float("nan"), device="cuda")
+    q4k.q4k_gate_up(dev(Wg), dev(Wu), dev(x), h, inter, hidden, q4k.Q4K_ACT_SILU)
+    torch.cuda.synchronize()
+    ref, Ah = _h_tolerance(orc, Wg, Wu, x, inter, hidden, orc.SILU)
+    assert_close(h.cpu().numpy(), ref, Ah, what="gate_up 20001x2560 (interleaved)")
+
+
+def test_interleaved_lmhead_topk(q4k, orc):
+    rng = np.random.default_rng(96)
+    rows, cols, k = 50001, 2560, 7
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols, scale=0.5)
+    ref, A = orc.matvec(W, x, rows, cols)
+    logits, ti, tv = gpu_lmhead(q4k, W, x, rows, cols, k)
+    assert_close(logits, ref, A, what="lm_head 50001x2560 (interleaved)")
+    topk_ok(ti, tv, ref, A, k)
+    gidx, _ = orc.topk(logits.astype(np.float64), k)
+    assert np.array_equal(ti, gidx)
+    # the last row (alone in the final sweep) can win
+    W2 = W.copy()
+    W2[rows - 1] = W[int(np.argmax(ref))]
+    W2[rows - 1, 0:2] = np.array([0x00, 0x3C], np.uint8)    # d = 1.0: a large logit
+    ref2, A2 = orc.matvec(W2, x, rows, cols)
+    logits2, ti2, tv2 = gpu_lmhead(q4k, W2, x, rows, cols, k)
+    topk_ok(ti2, tv2, ref2, A2, k)
+    l3, ti3, tv3, tp3, lse3 = gpu_lmhead_probs(q4k, W2, x, rows, cols, k)
+    assert np.array_equal(ti3, ti2)
+    check_probs(l3, ti3, tv3, tp3, lse3, ref2, A2, "probs 50001x2560 (interleaved)")
+
+
 # ------------------------------------------------- lm_head probabilities ---
 
 def gpu_lmhead_probs(q4k, W, x, rows, cols, k):
