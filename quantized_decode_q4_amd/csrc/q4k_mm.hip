@@ -189,6 +189,27 @@ __device__ __forceinline__ int b_pos(int n, int c, int j)
     return 16 * c + (n ^ ((j & 3) | (c << 2)));
 }
 
+// Weight bytes of one super-block for a workgroup of NT tiles (16 rows each),
+// and whether the LDS weight ring (three of them) fits beside the activation
+// ring and the shared-tile operand buffers.
+constexpr int w_stage_bytes(int nt) { return nt * 16 * kBlockBytes; }
+constexpr int b_buf_bytes(int b) { return b > 0 ? 2 * b * 8192 : 16; }
+constexpr bool lds_weights(int a, int b)
+{
+    // LDS budget, and the loader's prologue (two weight stages and one
+    // activation chunk of 32 loads) within the 63 outstanding loads of a wave
+    return kXBufs * kChunk + b_buf_bytes(b) + 3 * w_stage_bytes(4 * a + b) <= 160 * 1024 - 2048 &&
+           2 * ((w_stage_bytes(4 * a + b) / 16 + 63) / 64) + kChunk / 1024 <= 63;
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N <= 63 (expcnt / lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ void wait_vmcnt_le(int n)
 {
     // s_waitcnt with expcnt / lgkmcnt at their maxima (no wait on them).
@@ -260,13 +281,24 @@ __device__ __forceinline__ uint2 deq4(uint32_t w, float a, float b)
 // SIMD dequantise disjoint weights; their partial sums are added at the end.
 // Wave 8 is the loader: it copies the activation chunks of the next
 // super-blocks into a 3-deep LDS ring with LDS-DMA loads, on a wait counter
-// of its own, so the compute waves' weight prefetch (a register ring of
-// kRing - 1 super-blocks) never waits on it. One barrier per super-block.
+// of its own. Where it fits (LDS, and the loader's 63 outstanding loads) it
+// also copies each super-block's weight bytes into a 3-deep LDS ring and the
+// compute waves issue no global loads; otherwise they prefetch their weights
+// into a register ring of kRing - 1 super-blocks. One barrier per super-block.
 template <int NMAT, int A, int B>
 __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
 {
+    // With kWL the loader also copies each super-block's weight bytes (all of
+    // the workgroup's rows, 144 B each, in tile-row order) into a 3-deep LDS
+    // ring, so the compute waves issue no global loads at all.
+    constexpr int NT = 4 * A + B;
+    constexpr bool kWL = lds_weights(A, B);
+    constexpr int kWStage = w_stage_bytes(NT);
+    constexpr int kWPieces = NT * 16 * (kBlockBytes / 16);   // 16-byte pieces per stage
+    constexpr int kWInstr = (kWPieces + 63) / 64;            // loader instructions per stage
     __shared__ __attribute__((aligned(16))) uint8_t xbuf[kXBufs * kChunk];
-    __shared__ __attribute__((aligned(16))) uint8_t bbuf[2 * (B > 0 ? B : 1) * 8 * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t bbuf[b_buf_bytes(B)];
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf[kWL ? 3 * kWStage : 16];
 
     const int rg = blockIdx.x / p.S, sp = blockIdx.x % p.S;
     const int64_t tg = blockIdx.y;
@@ -288,12 +320,52 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
                 __builtin_amdgcn_global_load_lds((const void *)(s + i * 1024),
                                                  (lds_ptr)(dst + i * 1024), 16, 0, 0);
         };
-        issue(0);
-        if (nblk > 1) issue(1);
-        for (int b = 0; b < niter; ++b) {
-            if (b < nblk) wait_vmcnt_le(b + 1 < nblk ? 32 : 0);   // chunk b has landed
+        if constexpr (kWL) {
+            // Weights of block b go out before its activations, so that at
+            // barrier b only the activations of block b+1 may be in flight:
+            // block b+1's weights (staged for the shared tiles at the end of
+            // block b) have landed with block b's activations.
+            auto issue_w = [&](int b) {
+                const int64_t boff = (int64_t)(kb0 + b) * kBlockBytes;
+                uint8_t *dst = wbuf + (b % 3) * kWStage;
+#pragma unroll
+                for (int i = 0; i < kWInstr; ++i) {
+                    const int pc = i * 64 + l;
+                    if (pc < kWPieces) {
+                        const int row = pc / 9, piece = pc % 9;
+                        const uint8_t *srcw = row_ptr<NMAT>(p, tile0 + row / 16, row % 16) + boff + piece * 16;
+                        __builtin_amdgcn_global_load_lds((const void *)srcw, (lds_ptr)(dst + i * 1024), 16, 0, 0);
+                    }
+                }
+            };
+            // prologue: weights of blocks 0 and 1, then activations of block
+            // 0; once both weight stages have landed (only block 0's
+            // activations may still be in flight) the shared tiles of block 0
+            // can be staged, and block 1's activations go out. At most
+            // 2 * kWInstr + 32 <= 63 loads are outstanding here.
+            static_assert(2 * kWInstr + kChunk / 1024 <= 63, "loader wait counter");
+            issue_w(0);
+            if (nblk > 1) issue_w(1);
+            issue(0);
+            wait_vmcnt<kChunk / 1024>();
             barrier_lds();
-            if (b + 2 < nblk) issue(b + 2);   // into the buffer chunk b-1 used
+            if (nblk > 1) issue(1);
+            for (int b = 0; b < niter; ++b) {
+                if (b < nblk) wait_vmcnt_le(b + 1 < nblk ? 32 : 0);
+                barrier_lds();
+                if (b + 2 < nblk) {
+                    issue_w(b + 2);
+                    issue(b + 2);
+                }
+            }
+        } else {
+            issue(0);
+            if (nblk > 1) issue(1);
+            for (int b = 0; b < niter; ++b) {
+                if (b < nblk) wait_vmcnt_le(b + 1 < nblk ? 32 : 0);   // chunk b has landed
+                barrier_lds();
+                if (b + 2 < nblk) issue(b + 2);   // into the buffer chunk b-1 used
+            }
         }
         barrier_lds();   // the compute waves' two barriers of the pair reduction
         barrier_lds();
@@ -311,6 +383,27 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
     for (int s = 0; s < B; ++s) rp_sh[s] = row_ptr<NMAT>(p, tile0 + 4 * A + s, ns);
 
     Slot<A, B> ring[kRing];
+    // kWL: block b's weight bytes in the LDS ring; row rr of the workgroup
+    // (tile rr / 16, tile row rr % 16) starts at byte 144 rr of the stage.
+    auto wrow = [&](int b, int rr) -> const uint8_t * {
+        return wbuf + (b % 3) * kWStage + rr * kBlockBytes;
+    };
+    auto load_own_lds = [&](Slot<A, B> &sl, int b) {
+#pragma unroll
+        for (int i = 0; i < A; ++i) {
+            const uint8_t *r = wrow(b, (simd * A + i) * 16 + n);
+            sl.oh[i] = *reinterpret_cast<const uint4 *>(r);
+            sl.oq[i] = *reinterpret_cast<const uint4 *>(r + 16 + 32 * c + 16 * half);
+        }
+    };
+    auto load_sh_lds = [&](Slot<A, B> &sl, int b) {
+#pragma unroll
+        for (int s = 0; s < B; ++s) {
+            const uint8_t *r = wrow(b, (4 * A + s) * 16 + ns);
+            sl.sh[s] = *reinterpret_cast<const uint4 *>(r);
+            sl.sq[s] = *reinterpret_cast<const uint32_t *>(r + 16 + 4 * q4);
+        }
+    };
     auto load = [&](Slot<A, B> &sl, int b) {
         const int64_t off = (int64_t)(kb0 + min(b, nblk - 1)) * kBlockBytes;
 #pragma unroll
@@ -352,19 +445,31 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
 #pragma unroll
     for (int s = 0; s < B; ++s) acc_sh[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (kWL) {
+        barrier_lds();   // the loader has block 0's (and 1's) weights in LDS
+        if constexpr (B > 0) {
+            load_sh_lds(ring[0], 0);
+            stage(ring[0], 0);
+        }
+    } else {
 #pragma unroll
-    for (int b = 0; b < kRing - 1; ++b) load(ring[b], b);
-    // Keep all prologue loads ahead of the first wait (the scheduler would
-    // otherwise issue blocks 1.. only after block 0 has arrived).
-    asm volatile("" ::: "memory");
-    if constexpr (B > 0) stage(ring[0], 0);
+        for (int b = 0; b < kRing - 1; ++b) load(ring[b], b);
+        // Keep all prologue loads ahead of the first wait (the scheduler would
+        // otherwise issue blocks 1.. only after block 0 has arrived).
+        asm volatile("" ::: "memory");
+        if constexpr (B > 0) stage(ring[0], 0);
+    }
 
     for (int b0 = 0; b0 < niter; b0 += kRing) {
 #pragma unroll
         for (int u = 0; u < kRing; ++u) {
             const int b = b0 + u;
             barrier_lds();   // block b's activations and shared operands are in LDS
-            load(ring[(u + kRing - 1) % kRing], b + kRing - 1);
+            if constexpr (kWL) {
+                if (b < nblk) load_own_lds(ring[u], b);
+            } else {
+                load(ring[(u + kRing - 1) % kRing], b + kRing - 1);
+            }
             if (b < nblk) {
                 const uint8_t *xb = xbuf + (b % kXBufs) * kChunk;
                 const uint8_t *sbase = bbuf + ((b & 1) * B) * 8192;
@@ -413,7 +518,10 @@ __global__ __launch_bounds__(kThreads, 1) void mm_kernel(MmArgs p)
                         acc_sh[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.xa[0], o.wb[s], acc_sh[s], 0, 0, 0);
                 }
                 if constexpr (B > 0) {
-                    if (b + 1 < nblk) stage(ring[(u + 1) % kRing], (b + 1) & 1);
+                    if (b + 1 < nblk) {
+                        if constexpr (kWL) load_sh_lds(ring[(u + 1) % kRing], b + 1);
+                        stage(ring[(u + 1) % kRing], (b + 1) & 1);
+                    }
                 }
             }
         }
