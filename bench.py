@@ -184,6 +184,7 @@ def main() -> int:
     v = torch.empty(KVROWS, device=dev)
     y = torch.empty(HIDDEN, device=dev)
     h = q4k.workspace(q4k.q4k_ffn_workspace_bytes(HIDDEN, INTER))
+    hf = h.view(torch.float32)   # the same workspace as the f32 vector h (gate_up / down alone)
     logits = torch.empty(VOCAB, device=dev)
     top_idx = torch.empty(TOPK, dtype=torch.int32, device=dev)
     top_val = torch.empty(TOPK, device=dev)
@@ -264,9 +265,9 @@ def main() -> int:
     if args.kernel_only:
         # profiling helper: launch one kind of kernel over the 34 layers
         parts = {
-            "gate_up": lambda: [q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], h, INTER, HIDDEN, GELU)
+            "gate_up": lambda: [q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], hf, INTER, HIDDEN, GELU)
                                 for L in ffn_dev],
-            "down": lambda: [q4k.q4k_matvec(L["Wd"], h, y, HIDDEN, INTER) for L in ffn_dev],
+            "down": lambda: [q4k.q4k_matvec(L["Wd"], hf, y, HIDDEN, INTER) for L in ffn_dev],
             "qkv": lambda: [q4k.q4k_qkv(c["W"], c["x"], q, k, v, QROWS, KVROWS, HIDDEN)
                             for c in qkv_dev],
             "lmhead": run_lmhead,
@@ -362,7 +363,7 @@ def main() -> int:
     g_gu = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_gu):
         for L in ffn_dev:
-            q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], h, INTER, HIDDEN, GELU)
+            q4k.q4k_gate_up(L["Wg"], L["Wu"], L["x"], hf, INTER, HIDDEN, GELU)
     torch.cuda.synchronize()
     g_gu.replay()
     torch.cuda.synchronize()

@@ -90,6 +90,29 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _arg(t, name: str, nbytes: int, dtype=None, optional: bool = False) -> int | None:
+    """Address of a tensor argument after checking what the C call cannot:
+    that it is a contiguous device tensor of the expected dtype holding at
+    least `nbytes` bytes. Raw integer pointers are passed through unchecked
+    (the caller vouches for them); None is allowed only for optional ones."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call reads or writes {nbytes}")
+    return t.data_ptr()
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         import torch
@@ -108,18 +131,52 @@ def _check(status: int, where: str) -> None:
         raise Q4KError(status, where)
 
 
+def _blocks(n: int) -> int:
+    """Super-blocks per row (0 for a length the library will reject)."""
+    return n // 256 if n > 0 and n % 256 == 0 else 0
+
+
+def _wq4(rows: int, cols: int) -> int:
+    return max(rows, 0) * _blocks(cols) * 144
+
+
+def _wq6(rows: int, cols: int) -> int:
+    return max(rows, 0) * _blocks(cols) * 210
+
+
+def _f32(n: int) -> int:
+    return 4 * max(n, 0)
+
+
+def _colv(n: int) -> int:
+    """Bytes of an f32 vector whose length must be a positive multiple of 256
+    (0 when it is not: the C call reports the shape error itself)."""
+    return 4 * n if _blocks(n) else 0
+
+
+_U8, _FLOAT, _INT32 = torch.uint8, torch.float32, torch.int32
+
+
 def q4k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
-    _check(lib.q4k_matvec(_ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)), "q4k_matvec")
+    _check(lib.q4k_matvec(_arg(W, "W", _wq4(rows, cols), _U8), _arg(x, "x", _colv(cols), _FLOAT),
+                          _arg(y, "y", _f32(rows), _FLOAT), rows, cols, _stream(stream)),
+           "q4k_matvec")
 
 
 def q6k_matvec(W, x, y, rows: int, cols: int, stream=None) -> None:
-    _check(lib.q6k_matvec(_ptr(W), _ptr(x), _ptr(y), rows, cols, _stream(stream)), "q6k_matvec")
+    _check(lib.q6k_matvec(_arg(W, "W", _wq6(rows, cols), _U8), _arg(x, "x", _colv(cols), _FLOAT),
+                          _arg(y, "y", _f32(rows), _FLOAT), rows, cols, _stream(stream)),
+           "q6k_matvec")
 
 
 def q4k_rmsnorm_matvec(W, h, delta, norm_w, eps: float, h_out, y, rows: int, cols: int,
                        stream=None) -> None:
-    _check(lib.q4k_rmsnorm_matvec(_ptr(W), _ptr(h), _ptr(delta), _ptr(norm_w), float(eps),
-                                  _ptr(h_out), _ptr(y), rows, cols, _stream(stream)),
+    _check(lib.q4k_rmsnorm_matvec(_arg(W, "W", _wq4(rows, cols), _U8),
+                                  _arg(h, "h", _colv(cols), _FLOAT),
+                                  _arg(delta, "delta", _colv(cols), _FLOAT, optional=True),
+                                  _arg(norm_w, "norm_w", _colv(cols), _FLOAT), float(eps),
+                                  _arg(h_out, "h_out", _colv(cols), _FLOAT, optional=True),
+                                  _arg(y, "y", _f32(rows), _FLOAT), rows, cols, _stream(stream)),
            "q4k_rmsnorm_matvec")
 
 
@@ -127,20 +184,32 @@ def q4k_rmsnorm_ffn(Wg, Wu, Wd, h, delta, norm_w, eps: float, h_out, y, hidden: 
                     act: int, ws, ws_bytes: int | None = None, stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
-    _check(lib.q4k_rmsnorm_ffn(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(h), _ptr(delta), _ptr(norm_w),
-                               float(eps), _ptr(h_out), _ptr(y), hidden, inter, act, _ptr(ws),
-                               ws_bytes, _stream(stream)), "q4k_rmsnorm_ffn")
+    _check(lib.q4k_rmsnorm_ffn(_arg(Wg, "Wg", _wq4(inter, hidden), _U8),
+                               _arg(Wu, "Wu", _wq4(inter, hidden), _U8),
+                               _arg(Wd, "Wd", _wq4(hidden, inter), _U8),
+                               _arg(h, "h", _colv(hidden), _FLOAT),
+                               _arg(delta, "delta", _colv(hidden), _FLOAT, optional=True),
+                               _arg(norm_w, "norm_w", _colv(hidden), _FLOAT), float(eps),
+                               _arg(h_out, "h_out", _colv(hidden), _FLOAT, optional=True),
+                               _arg(y, "y", _colv(hidden), _FLOAT), hidden, inter, act,
+                               _arg(ws, "ws", ws_bytes), ws_bytes, _stream(stream)),
+           "q4k_rmsnorm_ffn")
 
 
 def q4k_qkv(Wqkv, x, q, k, v, q_rows: int, kv_rows: int, cols: int, stream=None) -> None:
-    _check(lib.q4k_qkv(_ptr(Wqkv), _ptr(x), _ptr(q), _ptr(k), _ptr(v), q_rows, kv_rows, cols,
+    rows = q_rows + 2 * kv_rows
+    _check(lib.q4k_qkv(_arg(Wqkv, "Wqkv", _wq4(rows, cols), _U8), _arg(x, "x", _colv(cols), _FLOAT),
+                       _arg(q, "q", _f32(q_rows), _FLOAT), _arg(k, "k", _f32(kv_rows), _FLOAT),
+                       _arg(v, "v", _f32(kv_rows), _FLOAT), q_rows, kv_rows, cols,
                        _stream(stream)), "q4k_qkv")
 
 
 def q4k_gate_up(Wg, Wu, x, h, inter: int, hidden: int, act: int = Q4K_ACT_GELU_TANH,
                 stream=None) -> None:
-    _check(lib.q4k_gate_up(_ptr(Wg), _ptr(Wu), _ptr(x), _ptr(h), inter, hidden, act,
-                           _stream(stream)), "q4k_gate_up")
+    _check(lib.q4k_gate_up(_arg(Wg, "Wg", _wq4(inter, hidden), _U8),
+                           _arg(Wu, "Wu", _wq4(inter, hidden), _U8),
+                           _arg(x, "x", _colv(hidden), _FLOAT), _arg(h, "h", _f32(inter), _FLOAT),
+                           inter, hidden, act, _stream(stream)), "q4k_gate_up")
 
 
 def q4k_ffn_workspace_bytes(hidden: int, inter: int) -> int:
@@ -151,8 +220,12 @@ def q4k_ffn(Wg, Wu, Wd, x, y, hidden: int, inter: int, act: int, ws, ws_bytes: i
             stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
-    _check(lib.q4k_ffn(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(x), _ptr(y), hidden, inter, act,
-                       _ptr(ws), ws_bytes, _stream(stream)), "q4k_ffn")
+    _check(lib.q4k_ffn(_arg(Wg, "Wg", _wq4(inter, hidden), _U8),
+                       _arg(Wu, "Wu", _wq4(inter, hidden), _U8),
+                       _arg(Wd, "Wd", _wq4(hidden, inter), _U8),
+                       _arg(x, "x", _colv(hidden), _FLOAT), _arg(y, "y", _colv(hidden), _FLOAT),
+                       hidden, inter, act, _arg(ws, "ws", ws_bytes), ws_bytes, _stream(stream)),
+           "q4k_ffn")
 
 
 def q4k_lmhead_workspace_bytes(rows: int, cols: int, k: int) -> int:
@@ -163,8 +236,12 @@ def q4k_lmhead_topk(W, x, logits, rows: int, cols: int, k: int, top_idx, top_val
                     ws_bytes: int | None = None, stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
-    _check(lib.q4k_lmhead_topk(_ptr(W), _ptr(x), _ptr(logits), rows, cols, k, _ptr(top_idx),
-                               _ptr(top_val), _ptr(ws), ws_bytes, _stream(stream)),
+    kk = max(k, 0)
+    _check(lib.q4k_lmhead_topk(_arg(W, "W", _wq4(rows, cols), _U8), _arg(x, "x", _colv(cols), _FLOAT),
+                               _arg(logits, "logits", _f32(rows), _FLOAT), rows, cols, k,
+                               _arg(top_idx, "top_idx", 4 * kk, _INT32),
+                               _arg(top_val, "top_val", _f32(kk), _FLOAT),
+                               _arg(ws, "ws", ws_bytes), ws_bytes, _stream(stream)),
            "q4k_lmhead_topk")
 
 
@@ -172,9 +249,15 @@ def q4k_lmhead_topk_probs(W, x, logits, rows: int, cols: int, k: int, top_idx, t
                           lse, ws, ws_bytes: int | None = None, stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
-    _check(lib.q4k_lmhead_topk_probs(_ptr(W), _ptr(x), _ptr(logits), rows, cols, k, _ptr(top_idx),
-                                     _ptr(top_val), _ptr(top_prob), _ptr(lse), _ptr(ws), ws_bytes,
-                                     _stream(stream)), "q4k_lmhead_topk_probs")
+    kk = max(k, 0)
+    _check(lib.q4k_lmhead_topk_probs(_arg(W, "W", _wq4(rows, cols), _U8),
+                                     _arg(x, "x", _colv(cols), _FLOAT),
+                                     _arg(logits, "logits", _f32(rows), _FLOAT), rows, cols, k,
+                                     _arg(top_idx, "top_idx", 4 * kk, _INT32),
+                                     _arg(top_val, "top_val", _f32(kk), _FLOAT),
+                                     _arg(top_prob, "top_prob", _f32(kk), _FLOAT),
+                                     _arg(lse, "lse", 4, _FLOAT), _arg(ws, "ws", ws_bytes),
+                                     ws_bytes, _stream(stream)), "q4k_lmhead_topk_probs")
 
 
 def q4k_matmul_workspace_bytes(rows: int, cols: int, seq: int) -> int:
@@ -185,8 +268,11 @@ def q4k_matmul(W, X, Y, rows: int, cols: int, seq: int, ws=None, ws_bytes: int |
                stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else _nbytes(ws)
-    _check(lib.q4k_matmul(_ptr(W), _ptr(X), _ptr(Y), rows, cols, seq, _ptr(ws), ws_bytes,
-                          _stream(stream)), "q4k_matmul")
+    _check(lib.q4k_matmul(_arg(W, "W", _wq4(rows, cols), _U8),
+                          _arg(X, "X", _colv(cols) * max(seq, 0), _FLOAT),
+                          _arg(Y, "Y", _f32(rows) * max(seq, 0), _FLOAT), rows, cols, seq,
+                          _arg(ws, "ws", ws_bytes, optional=True), ws_bytes, _stream(stream)),
+           "q4k_matmul")
 
 
 def q4k_ffn_prefill_workspace_bytes(seq: int, hidden: int, inter: int) -> int:
@@ -197,8 +283,13 @@ def q4k_ffn_prefill(Wg, Wu, Wd, X, Y, seq: int, hidden: int, inter: int, act: in
                     ws_bytes: int | None = None, stream=None) -> None:
     if ws_bytes is None:
         ws_bytes = _nbytes(ws)
-    _check(lib.q4k_ffn_prefill(_ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(X), _ptr(Y), seq, hidden, inter,
-                               act, _ptr(ws), ws_bytes, _stream(stream)), "q4k_ffn_prefill")
+    _check(lib.q4k_ffn_prefill(_arg(Wg, "Wg", _wq4(inter, hidden), _U8),
+                               _arg(Wu, "Wu", _wq4(inter, hidden), _U8),
+                               _arg(Wd, "Wd", _wq4(hidden, inter), _U8),
+                               _arg(X, "X", _colv(hidden) * max(seq, 0), _FLOAT),
+                               _arg(Y, "Y", _colv(hidden) * max(seq, 0), _FLOAT), seq, hidden,
+                               inter, act, _arg(ws, "ws", ws_bytes), ws_bytes, _stream(stream)),
+           "q4k_ffn_prefill")
 
 
 def q4k_status_string(status: int) -> str:

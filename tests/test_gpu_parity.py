@@ -525,8 +525,16 @@ def test_errors_raise_and_enqueue_nothing(q4k):
     with pytest.raises(q4k.Q4KError) as e:
         q4k.q4k_matvec(W, x, y, 10, 300)
     assert e.value.status == q4k.Q4K_ERR_SHAPE
-    with pytest.raises(q4k.Q4KError):
-        q4k.q4k_matvec(W, x, W, 10, 256)          # output aliases W
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_matvec(W, x, W.data_ptr(), 10, 256)   # output aliases W (raw pointer)
+    assert e.value.status == q4k.Q4K_ERR_ALIAS
+    # the binding itself rejects what the C call cannot see: sizes, dtypes, host memory
+    with pytest.raises(ValueError):
+        q4k.q4k_matvec(W, x, torch.empty(5, device="cuda"), 10, 256)     # y too short
+    with pytest.raises(ValueError):
+        q4k.q4k_matvec(W[:100], x, y, 10, 256)                            # W too short
+    with pytest.raises(ValueError):
+        q4k.q4k_matvec(W, x.double(), y, 10, 256)                         # wrong dtype
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
 
