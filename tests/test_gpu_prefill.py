@@ -134,6 +134,44 @@ def test_matmul_mfma_deterministic(q4k):
     assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
 
 
+def test_matmul_mfma_split_any_workspace_contents(q4k):
+    """A K-split launch keeps its bf16 activations and partial sums in the
+    workspace; whatever the workspace held before (zeros, garbage, the
+    previous call's data) the result is the same, bit for bit."""
+    rng = np.random.default_rng(74)
+    rows, cols, seq = 300, 10240, 64          # 40 splits along K
+    W, X = dev(inputs.q4k_random(rng, rows, cols)), dev(inputs.normal_f32(rng, (seq, cols)))
+    need = q4k.q4k_matmul_workspace_bytes(rows, cols, seq)
+    outs = []
+    for fill in (0, 255, 255, 7):
+        ws = q4k.workspace(need)
+        ws.fill_(fill)
+        Y = torch.full((seq, rows), float("nan"), device="cuda")
+        q4k.q4k_matmul(W, X, Y, rows, cols, seq, ws)
+        q4k.q4k_matmul(W, X, Y, rows, cols, seq, ws)   # again on the same workspace
+        torch.cuda.synchronize()
+        outs.append(Y.clone())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+
+
+def test_matmul_mfma_split_output_alignment(q4k):
+    """The K-split sum runs four outputs per thread when Y is 16-byte aligned
+    and one otherwise: both give the same bits."""
+    rng = np.random.default_rng(75)
+    rows, cols, seq = 300, 10240, 64
+    W, X = dev(inputs.q4k_random(rng, rows, cols)), dev(inputs.normal_f32(rng, (seq, cols)))
+    ws = q4k.workspace(q4k.q4k_matmul_workspace_bytes(rows, cols, seq))
+    buf = torch.full((seq * rows + 4,), float("nan"), device="cuda")
+    outs = []
+    for off in (0, 1):
+        Y = buf[off:off + seq * rows]
+        q4k.q4k_matmul(W, X, Y, rows, cols, seq, ws)
+        torch.cuda.synchronize()
+        outs.append(Y.clone())
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+
+
 def test_matmul_mfma_workspace_too_small(q4k):
     rows, cols, seq = 64, 256, 64
     need = q4k.q4k_matmul_workspace_bytes(rows, cols, seq)
@@ -156,6 +194,8 @@ FFN_SHAPES = [
     (256, 2560, 100, 0),
     (1024, 7680, 64, 1),
     (768, 1536, 65, 0),
+    (8192, 512, 64, 1),    # gate/up pair split along K (16 splits)
+    (4096, 512, 130, 0),   # ... with three token groups
 ]
 
 
