@@ -129,6 +129,8 @@ def main() -> int:
                     "copy that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill FFN leg")
     ap.add_argument("--no-q6k", action="store_true", help="skip the Q6_K matvec leg")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the leg at one GPU's share of an 8-way split")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -426,6 +428,56 @@ def main() -> int:
         }
         log(f"q6k matvec: {q6_us:.2f} us/call, {q6k_leg['gbs']:.0f} GB/s")
 
+    # ---------- one GPU's share of an 8-way tensor-parallel decode step
+    # QKV: 1 of 8 q heads and 1 of 4 kv heads (768 rows); FFN: 1280 of the
+    # 10240 inner rows (Wg/Wu rows, the matching Wd columns cut at super-block
+    # boundaries); lm_head: 32768 of the vocabulary rows. The collectives
+    # that would join the shards are not run (one GPU).
+    shard_leg = None
+    if not args.no_shard:
+        sp, qs, vs = INTER // 8, QROWS // 8, KVROWS // 4
+        sh = []
+        for l in range(LAYERS):
+            L, c = ffn_dev[l], qkv_dev[l]
+            Wd = L["Wd"].view(HIDDEN, INTER // 256, 144)[:, :sp // 256, :].reshape(HIDDEN, -1)
+            Wq = torch.cat([c["W"][:qs], c["W"][QROWS:QROWS + vs],
+                            c["W"][QROWS + KVROWS:QROWS + KVROWS + vs]])
+            sh.append({"Wg": L["Wg"][:sp], "Wu": L["Wu"][:sp], "Wd": Wd.contiguous(), "Wq": Wq,
+                       "x": L["x"]})
+        s_ws = q4k.workspace(q4k.q4k_ffn_workspace_bytes(HIDDEN, sp))
+        s_q, s_k, s_v = (torch.empty(n, device=dev) for n in (qs, vs, vs))
+        s_y = torch.empty(HIDDEN, device=dev)
+        lm_rows = VOCAB // 8
+        s_lm_ws = q4k.workspace(q4k.q4k_lmhead_workspace_bytes(lm_rows, HIDDEN, TOPK))
+        s_logits = torch.empty(lm_rows, device=dev)
+
+        def run_shard_layers():
+            for c in sh:
+                q4k.q4k_qkv(c["Wq"], c["x"], s_q, s_k, s_v, qs, vs, HIDDEN)
+                q4k.q4k_ffn(c["Wg"], c["Wu"], c["Wd"], c["x"], s_y, HIDDEN, sp, GELU, s_ws)
+
+        def run_shard_lm():
+            q4k.q4k_lmhead_topk_probs(lm_dev["W"][:lm_rows], lm_dev["x"], s_logits, lm_rows, HIDDEN,
+                                      TOPK, top_idx, top_val, top_prob, lse, s_lm_ws)
+
+        run_shard_layers()
+        run_shard_lm()
+        torch.cuda.synchronize()
+        s_layer_us = time_graph(run_shard_layers, 1) / LAYERS
+        s_lm_us = time_graph(run_shard_lm, 10)
+        s_bytes = (QROWS // 8 + 2 * (KVROWS // 4)) * HIDDEN // 256 * 144 + 3 * sp * HIDDEN // 256 * 144
+        shard_leg = {
+            "workload": "one GPU's share of an 8-way tensor-parallel decode step: QKV 768x2560 "
+                        "(1 q head + 1 kv head), FFN gate/up 2 x 1280x2560 and down 2560x1280, "
+                        "lm_head 32768x2560 top-5 with probabilities; collectives not run",
+            "us_per_layer": round(s_layer_us, 3),
+            "layer_gbs": round(s_bytes / (s_layer_us * 1e-6) / 1e9, 1),
+            "bytes_per_layer": s_bytes,
+            "lm_head_us": round(s_lm_us, 3),
+        }
+        log(f"8-way shard: {s_layer_us:.2f} us/layer (QKV + FFN), lm_head {s_lm_us:.2f} us")
+        del sh
+
     # ------------------------------------------ prefill FFN (matrix cores)
     prefill = None
     if do_prefill:
@@ -520,6 +572,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "prefill": prefill,
         "q6k_matvec": q6k_leg,
+        "tp8_shard": shard_leg,
     }
     print(json.dumps(rec), flush=True)
     return 0
