@@ -185,18 +185,22 @@ size_t q4k_matmul_workspace_bytes(int64_t rows, int64_t cols, int64_t seq);
 /* Small-batch matmul for prefill: Y[t][i] = sum_j W[i][j] X[t][j],
  * X: f32[seq][cols], Y: f32[seq][rows] (token-major). seq >= 64 runs on the
  * matrix cores with bf16 operands (weights dequantised to bf16 tiles in LDS,
- * fp32 accumulation); smaller seq runs the f32 matvec once per token.
+ * fp32 accumulation); smaller seq runs the f32 matvec of every token in one
+ * launch (the same per-row arithmetic as q4k_matvec, so each Y row equals
+ * q4k_matvec of that token bit for bit).
  * Source: infer-compute README, "Quick Start" (GPU prefill for seq > 1). */
 int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows, int64_t cols,
                int64_t seq, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace of q4k_ffn_prefill. */
+/* Workspace of q4k_ffn_prefill (seq < 64: h for every token, f32[seq][inter]). */
 size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, int64_t inter);
 
 /* Gated FFN for seq tokens: H = act(X Wg^T) * (X Wu^T), Y = H Wd^T.
  * X, Y: f32[seq][hidden]. seq >= 64: bf16 matrix-core path with the gated
  * activation applied to fp32 G/U before H is rounded to bf16; smaller seq:
- * q4k_ffn per token. Source: infer-compute README, "Quick Start" (prefill)
+ * the f32 gate+up of every token in one launch, then the down projection of
+ * every token in one launch (each Y row equals q4k_ffn of that token bit for
+ * bit). Source: infer-compute README, "Quick Start" (prefill)
  * and "Shaders" table (Q4_K fused FFN row). */
 int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, const float *X, float *Y,
                     int64_t seq, int64_t hidden, int64_t inter, int act,

@@ -330,20 +330,18 @@ Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows,
         return hip_status(q4k::launch_matmul_mfma((const uint8_t *)W, X, Y, rows, cols, seq,
                                                   (uint8_t *)ws, s));
     }
-    // f32 path: one matvec per token (every token re-reads W).
-    for (int64_t t = 0; t < seq; ++t) {
-        const int st = hip_status(q4k::launch_rows_store((const uint8_t *)W, X + t * cols,
-                                                         Y + t * rows, nullptr, nullptr, rows,
-                                                         cols, rows, rows, s));
-        if (st != Q4K_OK) return st;
-    }
-    return Q4K_OK;
+    // f32 path: the matvec of every token in one launch (grid row = token;
+    // the tokens after the first read W mostly from cache).
+    return hip_status(q4k::launch_rows_store((const uint8_t *)W, X, Y, nullptr, nullptr, rows, cols,
+                                             rows, rows, s, nullptr,
+                                             q4k::Batch{seq, cols, rows}));
 }
 
 Q4K_EXPORT size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, int64_t inter)
 {
     if (seq < 0 || !cols_ok(hidden) || !cols_ok(inter)) return 0;
-    size_t need = round_up((size_t)inter * 4, 256);
+    // f32 path: h for every token; matrix-core path: its own layout
+    size_t need = round_up((size_t)inter * 4 * (size_t)(seq >= 1 && seq < kMfmaMinSeq ? seq : 1), 256);
     if (seq >= kMfmaMinSeq && seq <= kSeqMax) {
         const size_t mm = (size_t)q4k::mm_ffn_workspace(seq, hidden, inter);
         need = mm > need ? mm : need;
@@ -377,12 +375,8 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
                                                        (const uint8_t *)Wd, X, Y, seq, hidden,
                                                        inter, act, (uint8_t *)ws, s));
     }
-    for (int64_t t = 0; t < seq; ++t) {
-        const int st = hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
-                                                  (const uint8_t *)Wd, X + t * hidden,
-                                                  Y + t * hidden, hidden, inter, act,
-                                                  (float *)ws, s));
-        if (st != Q4K_OK) return st;
-    }
-    return Q4K_OK;
+    // f32 path: gate+up for every token in one launch, then down likewise
+    return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                      (const uint8_t *)Wd, X, Y, hidden, inter, act, (float *)ws,
+                                      s, nullptr, seq));
 }

@@ -30,18 +30,26 @@ struct NormIn {
 };
 
 // Row-streaming kernels (q4k_rows.hip).
+// A batch of nvec activation vectors in one launch: vector v reads
+// x + v * x_stride and writes o0 + v * o_stride (no norm, no o1/o2 split).
+struct Batch {
+    int64_t nvec = 1;
+    int64_t x_stride = 0;
+    int64_t o_stride = 0;
+};
 // y rows [0, split0) -> o0, [split0, split1) -> o1, [split1, rows) -> o2.
 hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float *o1, float *o2,
                              int64_t rows, int64_t cols, int64_t split0, int64_t split1,
-                             hipStream_t s, const NormIn *norm = nullptr);
+                             hipStream_t s, const NormIn *norm = nullptr, const Batch &bt = Batch{});
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
                           int64_t rows, int64_t cols, int act, hipStream_t s,
-                          const NormIn *norm = nullptr);
+                          const NormIn *norm = nullptr, const Batch &bt = Batch{});
 // Gated FFN: gate+up with the activation applied (h, f32[inter]), then the
-// down projection reading h. A norm applies to the gate+up input.
+// down projection reading h. A norm applies to the gate+up input. nvec > 1
+// (no norm): x [nvec][hidden], h [nvec][inter], y [nvec][hidden].
 hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
                       float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s,
-                      const NormIn *norm = nullptr);
+                      const NormIn *norm = nullptr, int64_t nvec = 1);
 // Q6_K matvec (GGUF Q6_K rows, 210 bytes per 256 weights): y = W x.
 hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t rows,
                              int64_t cols, hipStream_t s);

@@ -150,6 +150,10 @@ struct RowsArgs {
     int32_t k;
     int32_t chunk;           // sweeps per unit of the workgroup split
     int32_t ilv;             // 1: workgroup w takes sweeps w, w+G, w+2G, ... (else a contiguous range)
+    // Several activation vectors in one launch (grid row y = vector y): x
+    // and o0 advance by these many floats per vector (o1, o2 unused then).
+    int64_t x_stride;
+    int64_t o_stride;
 };
 
 __device__ __forceinline__ float act_apply(float z, int act)
@@ -611,6 +615,11 @@ __device__ __forceinline__ float block_sum_f32(float v, float *scratch)
 template <int RPS, int NMAT, int EPI, int XS, int MAXT, int D, int FMT = FMT_Q4K>
 __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 {
+    // Grid row y works on the y-th activation vector of a batch (one vector:
+    // y = 0). The rows a workgroup streams depend only on blockIdx.x, so the
+    // vectors after the first read the same rows, mostly from cache.
+    a.x += (int64_t)blockIdx.y * a.x_stride;
+    a.o0 += (int64_t)blockIdx.y * a.o_stride;
     static_assert(RPS >= 1 && RPS <= 64 && (64 % RPS) == 0, "RPS must divide 64");
     static_assert(FMT == FMT_Q4K || (XS == XS_F32 && NMAT == 1),
                   "Q6_K: f32 activations, one matrix");
@@ -1210,7 +1219,8 @@ int device_cus()
 }
 
 template <int NMAT, int EPI, int XS, int D, int FMT = FMT_Q4K>
-hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hipStream_t s)
+hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hipStream_t s,
+                       int64_t nvec = 1)
 {
     // Long launches (at least kIlvMinSweeps sweeps per workgroup) interleave
     // their sweeps across workgroups: lm_head 80.6 -> 78.3 us, while the
@@ -1222,7 +1232,8 @@ hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hi
              a.rows * (int64_t)a.nb * fmt_block_bytes(FMT) <= ((int64_t)1 << 30))
                 ? 1
                 : 0;
-    const dim3 grid((unsigned)nwg), block((unsigned)threads);
+    if (nvec < 1 || nvec > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nwg, (unsigned)nvec), block((unsigned)threads);
     const int64_t cols = (int64_t)a.nb * kQK;
     const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols)
                        : (a.nw && XS == XS_F32 && cols <= kNormLdsCols) ? (size_t)(cols * 4)
@@ -1254,11 +1265,12 @@ hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hi
 // Block-floating-point activations: converted in LDS when they fit, else per
 // thread.
 template <int NMAT, int EPI, int D>
-hipError_t launch_rows_bfp(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s)
+hipError_t launch_rows_bfp(const RowsArgs &a, int rps, int threads, int64_t nwg, hipStream_t s,
+                           int64_t nvec = 1)
 {
     if ((int64_t)a.nb * kQK <= kLdsColsMax)
-        return launch_rows<NMAT, EPI, XS_LDS, D>(a, rps, threads, nwg, s);
-    return launch_rows<NMAT, EPI, XS_THREAD, D>(a, rps, threads, nwg, s);
+        return launch_rows<NMAT, EPI, XS_LDS, D>(a, rps, threads, nwg, s, nvec);
+    return launch_rows<NMAT, EPI, XS_THREAD, D>(a, rps, threads, nwg, s, nvec);
 }
 
 RowsArgs base_args(int64_t rows, int64_t cols)
@@ -1303,10 +1315,13 @@ void set_norm(RowsArgs &a, const NormIn *norm)
 
 hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float *o1, float *o2,
                              int64_t rows, int64_t cols, int64_t split0, int64_t split1,
-                             hipStream_t s, const NormIn *norm)
+                             hipStream_t s, const NormIn *norm, const Batch &bt)
 {
+    if (bt.nvec > 1 && (norm || split0 != rows)) return hipErrorInvalidValue;
     RowsArgs a = base_args(rows, cols);
     set_norm(a, norm);
+    a.x_stride = bt.x_stride;
+    a.o_stride = bt.o_stride;
     a.W0 = W;
     a.x = x;
     a.o0 = o0;
@@ -1320,16 +1335,21 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     // few sweeps per workgroup: f32 activations, no shared conversion step
     const int64_t sweeps = (rows + sh.rps - 1) / sh.rps;
     if (sweeps <= (int64_t)Q4K_STORE_F32_SWEEPS * nwg)
-        return launch_rows<1, EPI_STORE, XS_F32, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s);
+        return launch_rows<1, EPI_STORE, XS_F32, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s,
+                                                              bt.nvec);
 #endif
-    return launch_rows_bfp<1, EPI_STORE, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s);
+    return launch_rows_bfp<1, EPI_STORE, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s, bt.nvec);
 }
 
 hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *h,
-                          int64_t rows, int64_t cols, int act, hipStream_t s, const NormIn *norm)
+                          int64_t rows, int64_t cols, int act, hipStream_t s, const NormIn *norm,
+                          const Batch &bt)
 {
+    if (bt.nvec > 1 && norm) return hipErrorInvalidValue;
     RowsArgs a = base_args(rows, cols);
     set_norm(a, norm);
+    a.x_stride = bt.x_stride;
+    a.o_stride = bt.o_stride;
     a.W0 = Wg;
     a.W1 = Wu;
     a.x = x;
@@ -1337,23 +1357,27 @@ hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, 
     a.act = act;
     const Shape sh = pick_shape(cols);
     return launch_rows_bfp<2, EPI_GATE_UP, Q4K_GATE_UP_D>(
-        a, sh.rps, sh.threads, grid_for(rows, cols, sh, Q4K_GATE_UP_WGS_PER_CU), s);
+        a, sh.rps, sh.threads, grid_for(rows, cols, sh, Q4K_GATE_UP_WGS_PER_CU), s, bt.nvec);
 }
 
 hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
                       float *y, int64_t hidden, int64_t inter, int act, float *h, hipStream_t s,
-                      const NormIn *norm)
+                      const NormIn *norm, int64_t nvec)
 {
-    hipError_t e = launch_gate_up(Wg, Wu, x, h, inter, hidden, act, s, norm);
+    // nvec tokens: x [nvec][hidden] -> h [nvec][inter] -> y [nvec][hidden]
+    hipError_t e = launch_gate_up(Wg, Wu, x, h, inter, hidden, act, s, norm,
+                                  Batch{nvec, hidden, inter});
     if (e != hipSuccess) return e;
     // down projection: few rows per thread, so f32 activations (no conversion)
     RowsArgs b = base_args(hidden, inter);
     b.W0 = Wd;
     b.x = h;
     b.o0 = y;
+    b.x_stride = inter;
+    b.o_stride = hidden;
     const Shape sd = pick_shape(inter);
     return launch_rows<1, EPI_STORE, XS_F32, Q4K_DOWN_D>(
-        b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s);
+        b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s, nvec);
 }
 
 hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t rows,

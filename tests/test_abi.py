@@ -197,6 +197,9 @@ def test_prefill_validation():
     need = q4k.q4k_ffn_prefill_workspace_bytes(64, 256, 512)
     assert need >= 64 * 256 * 2 + 64 * 512 * 2
     assert q4k.q4k_ffn_prefill_workspace_bytes(3, 256, 512) >= 512 * 4
+    # below 64 tokens h is kept for every token
+    assert q4k.q4k_ffn_prefill_workspace_bytes(5, 256, 512) == 5 * 512 * 4
+    assert q4k.q4k_ffn_prefill_workspace_bytes(63, 256, 1024) == 63 * 1024 * 4
     assert L.q4k_ffn_prefill(A, B, C, D, E, 64, 256, 512, 3, F, need, S) == q4k.Q4K_ERR_ACT
     assert L.q4k_ffn_prefill(A, B, C, D, E, 64, 256, 512, 0, F, need - 1, S) == q4k.Q4K_ERR_WORKSPACE
     assert L.q4k_ffn_prefill(A, B, C, D, E, 0, 256, 512, 0, None, 0, S) == q4k.Q4K_OK

@@ -518,6 +518,52 @@ def test_ffn_prefill_small_seq(q4k, orc):
     assert_close(Y.cpu().numpy(), ref, A, what="ffn_prefill seq=3")
 
 
+# rows, cols, seq: the f32 matvec paths (f32 activations for few sweeps per
+# workgroup, LDS block floating point, per-thread block floating point for
+# rows wider than 16384, one row per sweep past 32768), 2 to 63 tokens
+SMALL_SEQ_SHAPES = [(300, 1024, 2), (4096, 2560, 5), (20000, 2560, 6), (1000, 10240, 63),
+                    (3000, 20480, 7), (40, 40960, 3), (7, 256, 33)]
+
+
+@pytest.mark.parametrize("rows,cols,seq", SMALL_SEQ_SHAPES)
+def test_matmul_small_seq_rows_equal_matvec(q4k, rows, cols, seq):
+    """Below 64 tokens every token's matvec runs in one launch; each Y row is
+    q4k_matvec of that token, bit for bit."""
+    print(f"matmul small seq rows={rows} cols={cols} seq={seq}", flush=True)
+    rng = np.random.default_rng(rows + cols + seq)
+    W = dev(inputs.q4k_random(rng, rows, cols))
+    X = dev(inputs.normal_f32(rng, (seq, cols)))
+    Y = torch.full((seq, rows), float("nan"), device="cuda")
+    q4k.q4k_matmul(W, X, Y, rows, cols, seq)
+    ref = torch.full((seq, rows), float("nan"), device="cuda")
+    for t in range(seq):
+        q4k.q4k_matvec(W, X[t], ref[t], rows, cols)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("hidden,inter,seq,act", [(512, 768, 2, 0), (2560, 10240, 5, 0),
+                                                  (1024, 3072, 63, 1), (256, 20480, 4, 1)])
+def test_ffn_prefill_small_seq_rows_equal_ffn(q4k, hidden, inter, seq, act):
+    """Below 64 tokens the FFN runs as one gate+up launch and one down launch
+    for all tokens; each Y row is q4k_ffn of that token, bit for bit."""
+    print(f"ffn_prefill small seq hidden={hidden} inter={inter} seq={seq}", flush=True)
+    rng = np.random.default_rng(hidden + inter + seq)
+    Wg = dev(inputs.q4k_random(rng, inter, hidden))
+    Wu = dev(inputs.q4k_random(rng, inter, hidden))
+    Wd = dev(inputs.q4k_random(rng, hidden, inter))
+    X = dev(inputs.normal_f32(rng, (seq, hidden)))
+    Y = torch.full((seq, hidden), float("nan"), device="cuda")
+    q4k.q4k_ffn_prefill(Wg, Wu, Wd, X, Y, seq, hidden, inter, act,
+                        q4k.workspace(q4k.q4k_ffn_prefill_workspace_bytes(seq, hidden, inter)))
+    ref = torch.full((seq, hidden), float("nan"), device="cuda")
+    ws = q4k.workspace(q4k.q4k_ffn_workspace_bytes(hidden, inter))
+    for t in range(seq):
+        q4k.q4k_ffn(Wg, Wu, Wd, X[t], ref[t], hidden, inter, act, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int32), ref.view(torch.int32))
+
+
 def test_errors_raise_and_enqueue_nothing(q4k):
     y = torch.full((10,), 7.0, device="cuda")
     W = torch.zeros(10 * 144, dtype=torch.uint8, device="cuda")
