@@ -88,6 +88,12 @@
 #ifndef Q4K_INTERLEAVE
 #define Q4K_INTERLEAVE 1            // long launches: workgroups take every G-th sweep
 #endif
+#ifndef Q4K_WAVE_LOCAL_X
+#define Q4K_WAVE_LOCAL_X 1          // each wave converts the activations its own units use
+#endif
+#ifndef Q4K_DPP_QUAD
+#define Q4K_DPP_QUAD 1              // quad max/sum of the conversion with DPP instead of LDS permutes
+#endif
 #ifndef Q6K_D
 #define Q6K_D 1                     // sweeps in flight, Q6_K matvec
 #endif
@@ -532,6 +538,12 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ uint64_t join_u64(uint32_t hi, uint32_t lo)
 {
     return ((uint64_t)hi << 32) | lo;
@@ -698,8 +710,28 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     uint4 xv[XS == XS_LDS ? 2 : 16];
     uint32_t xoff[XS == XS_LDS ? 1 : 16];
     uint4 nv[XS == XS_LDS ? 4 : 6];   // norm inputs issued with x (see above)
+    // XS_LDS group mapping. Without a norm (no row-wide sum of squares), each
+    // wave converts exactly the gpw = 512/RPS groups of 8 activations its own
+    // units read (units 64w/RPS .. 64(w+1)/RPS - 1), lane l taking groups
+    // gbase + l + 64i, so no workgroup barrier is needed before the planes are
+    // read: LDS accesses of one wave complete in order. With a norm, thread t
+    // takes groups t, t + blockDim, ... and a barrier publishes the planes.
+    const bool wave_local = Q4K_WAVE_LOCAL_X && XS == XS_LDS && a.nw == nullptr;
+    const int gpw = 512 / RPS;
+    const int gbase = wave * gpw;
+    const int gpasses = wave_local ? (gpw + 63) / 64 : (ngroups + (int)blockDim.x - 1) / (int)blockDim.x;
+    // group of pass i of this thread, or ngroups for none
+    auto group_of = [&](int i) -> int {
+        if (wave_local) {
+            const int l = lane + 64 * i;
+            return (l < gpw && gbase + l < ngroups) ? gbase + l : ngroups;
+        }
+        const int e = t + i * (int)blockDim.x;
+        return e < ngroups ? e : ngroups;
+    };
     if (XS == XS_LDS) {
-        const uint32_t xo = t < ngroups ? (uint32_t)t * 32u : kOutOfRange;
+        const int e0 = group_of(0);
+        const uint32_t xo = e0 < ngroups ? (uint32_t)e0 * 32u : kOutOfRange;
         xv[0] = bload16(rx, xo);
         xv[1] = bload16(rx, xo + 16u);
         if (norm) {
@@ -850,7 +882,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         }
     } else {
         // Cooperative conversion: 4 threads per 32-activation sub-block, 8
-        // activations each; max and sum over the 4 lanes by xor shuffles.
+        // activations each; max and sum over the 4 lanes of a quad (DPP).
         float *Xs = reinterpret_cast<float *>(xlds + 3 * cols);
         float *Ss = Xs + cols / 32;
         // group e of 8 activations (x, and with a norm delta and nw, given)
@@ -876,10 +908,18 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 amax = fmaxf(amax, fabsf(v[i]));
                 sum += v[i];
             }
+#if Q4K_DPP_QUAD
+            // quad_perm [1,0,3,2] and [2,3,0,1]: lane ^ 1, lane ^ 2
+            amax = fmaxf(amax, dpp_f32<0xB1>(amax));
+            sum += dpp_f32<0xB1>(sum);
+            amax = fmaxf(amax, dpp_f32<0x4E>(amax));
+            sum += dpp_f32<0x4E>(sum);
+#else
             amax = fmaxf(amax, __shfl_xor(amax, 1));
             sum += __shfl_xor(sum, 1);
             amax = fmaxf(amax, __shfl_xor(amax, 2));
             sum += __shfl_xor(sum, 2);
+#endif
             int shift;
             float X;
             bfp_params(amax, sum, shift, X);
@@ -905,10 +945,10 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         // wider than 8 * blockDim) are loaded here. Trip counts are uniform
         // (blockDim % 4 == 0), so the xor shuffles see whole quads.
         const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-        convert(t, xv[0], xv[1], norm ? nv[0] : zero4, norm ? nv[1] : zero4,
+        convert(group_of(0), xv[0], xv[1], norm ? nv[0] : zero4, norm ? nv[1] : zero4,
                 norm ? nv[2] : zero4, norm ? nv[3] : zero4);
-        for (int e0 = blockDim.x; e0 < ngroups; e0 += blockDim.x) {
-            const int e = e0 + t;
+        for (int i = 1; i < gpasses; ++i) {
+            const int e = group_of(i);
             const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
             const uint4 h0 = bload16(rx, xo), h1 = bload16(rx, xo + 16u);
             uint4 d0 = zero4, d1 = zero4, w0 = zero4, w1 = zero4;
@@ -923,6 +963,11 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         if (norm) {
             const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes the planes
             inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
+        } else if (wave_local) {
+            // the wave reads back only what it wrote: keep the compiler from
+            // moving the reads above the writes
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         } else {
             __syncthreads();
         }
