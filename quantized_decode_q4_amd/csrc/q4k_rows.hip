@@ -68,7 +68,7 @@
 #define Q4K_STORE_WGS_PER_CU 1
 #endif
 #ifndef Q4K_STORE_F32_SWEEPS
-#define Q4K_STORE_F32_SWEEPS 2      // sweeps per workgroup up to which matvec uses f32 activations
+#define Q4K_STORE_F32_SWEEPS 2      // sweeps per workgroup (x 8/RPS) up to which matvec uses f32 activations
 #endif
 #ifndef Q4K_GATE_UP_D
 #define Q4K_GATE_UP_D 1
@@ -707,7 +707,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const bool z_lds = norm && XS == XS_F32 && cols <= kNormLdsCols;
     const __amdgpu_buffer_rsrc_t rdel = make_rsrc(a.delta, a.delta ? (uint32_t)(cols * 4) : 0u);
     const __amdgpu_buffer_rsrc_t rnw = make_rsrc(a.nw, norm ? (uint32_t)(cols * 4) : 0u);
-    uint4 xv[XS == XS_LDS ? 2 : 16];
+    // XS_LDS without a norm: the activations of the first kXPre conversion
+    // passes are all loaded up front (one memory latency instead of one per
+    // pass; rows of 2048 or more columns at RPS <= 2 take several passes).
+    constexpr int kWlPasses = (512 / RPS + 63) / 64;
+    constexpr int kXPre = kWlPasses < 4 ? kWlPasses : 4;
+    uint4 xv[XS == XS_LDS ? 2 * kXPre : 16];
     uint32_t xoff[XS == XS_LDS ? 1 : 16];
     uint4 nv[XS == XS_LDS ? 4 : 6];   // norm inputs issued with x (see above)
     // XS_LDS group mapping. Without a norm (no row-wide sum of squares), each
@@ -739,6 +744,14 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             nv[1] = bload16(rdel, xo + 16u);
             nv[2] = bload16(rnw, xo);
             nv[3] = bload16(rnw, xo + 16u);
+        } else {
+#pragma unroll
+            for (int i = 1; i < kXPre; ++i) {
+                const int e = group_of(i);
+                const uint32_t xoi = (wave_local && e < ngroups) ? (uint32_t)e * 32u : kOutOfRange;
+                xv[2 * i] = bload16(rx, xoi);
+                xv[2 * i + 1] = bload16(rx, xoi + 16u);
+            }
         }
     } else {
         if (FMT == FMT_Q6K) {
@@ -947,7 +960,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
         convert(group_of(0), xv[0], xv[1], norm ? nv[0] : zero4, norm ? nv[1] : zero4,
                 norm ? nv[2] : zero4, norm ? nv[3] : zero4);
-        for (int i = 1; i < gpasses; ++i) {
+        if (wave_local) {
+#pragma unroll
+            for (int i = 1; i < kXPre; ++i)
+                convert(group_of(i), xv[2 * i], xv[2 * i + 1], zero4, zero4, zero4, zero4);
+        }
+        for (int i = wave_local ? kXPre : 1; i < gpasses; ++i) {
             const int e = group_of(i);
             const uint32_t xo = e < ngroups ? (uint32_t)e * 32u : kOutOfRange;
             const uint4 h0 = bload16(rx, xo), h1 = bload16(rx, xo + 16u);
@@ -1377,9 +1395,14 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     const Shape sh = pick_shape(cols);
     const int64_t nwg = grid_for(rows, cols, sh, Q4K_STORE_WGS_PER_CU);
 #if Q4K_STORE_F32_SWEEPS > 0
-    // few sweeps per workgroup: f32 activations, no shared conversion step
+    // few sweeps per workgroup: f32 activations, no shared conversion step.
+    // The conversion takes 8/RPS passes per thread (wider rows, fewer rows per
+    // sweep), so the sweep count it pays off at grows with it: at 2560x10240
+    // (RPS 2, 5 sweeps per workgroup) f32 7.4 us against 7.9 us, at
+    // 16384x2560 (RPS 8, 8 sweeps) block floating point 8.1 us against 8.8 us.
     const int64_t sweeps = (rows + sh.rps - 1) / sh.rps;
-    if (sweeps <= (int64_t)Q4K_STORE_F32_SWEEPS * nwg)
+    const int64_t f32_sweeps = (int64_t)Q4K_STORE_F32_SWEEPS * (sh.rps < 8 ? 8 / sh.rps : 1);
+    if (sweeps <= f32_sweeps * nwg)
         return launch_rows<1, EPI_STORE, XS_F32, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s,
                                                               bt.nvec);
 #endif

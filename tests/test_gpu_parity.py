@@ -90,6 +90,19 @@ def test_matvec_ragged_shapes(q4k, orc, rows, cols):
     assert_close(y, ref, A, what=f"matvec {rows}x{cols}")
 
 
+# Wide rows with enough sweeps per workgroup for block-floating-point
+# activations converted over several wave-local passes (RPS 4, 2, 1: 2, 4 and 8
+# passes, the first four loaded up front), each with a ragged last sweep.
+@pytest.mark.parametrize("rows,cols", [(6001, 5120), (8195, 10240), (5003, 16384)])
+def test_matvec_wide_rows_multipass_conversion(q4k, orc, rows, cols):
+    rng = np.random.default_rng(rows * 104729 + cols)
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    y = gpu_matvec(q4k, W, x, rows, cols)
+    ref, A = orc.matvec(W, x, rows, cols)
+    assert_close(y, ref, A, what=f"matvec {rows}x{cols}")
+
+
 def test_matvec_crafted_fields(q4k, orc):
     """Zero nibbles, zero d, saturated fields and extreme binary16 scales."""
     rng = np.random.default_rng(21)
