@@ -5,8 +5,10 @@ independently seeded layers the fused QKV projection (4096 x 2560) and the
 gated FFN (gate+up 2 x 10240 x 2560 -> GELU-tanh -> down 2560 x 10240), then the
 lm_head (262144 x 2560) with top-5 and their softmax probabilities. All weights (2.1 GB) are resident in HBM
 before timing; 34 distinct layers exceed the 256 MB Infinity Cache, so each
-step streams its weights from HBM. Steps are replayed from HIP graphs captured
-once (launch-bound inner loop); the eager launch rate is reported beside it.
+step streams its weights from HBM. Each step is one replay of a HIP graph of the
+whole step captured once (launch-bound inner loop), and the timed region holds
+nothing else; the layers / lm_head split comes from a second pass with HIP
+events, and eager launches of the same step are timed beside it.
 
 Beside the step: the full Q4_K sequence of a layer (QKV, the attention output
 projection 2560 x 2048, FFN) over the 34 layers; the Q6_K matvec at the
@@ -289,15 +291,24 @@ def main() -> int:
     torch.cuda.synchronize()
     use_graph = not args.no_graph
     if use_graph:
+        # the whole step as one graph (timed), and its two parts as graphs of
+        # their own (for the layers / lm_head split, timed separately)
+        g_step = torch.cuda.CUDAGraph()
         g_layers = torch.cuda.CUDAGraph()
         g_lm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            run_layers()
+            run_lmhead()
         with torch.cuda.graph(g_layers):
             run_layers()
         with torch.cuda.graph(g_lm):
             run_lmhead()
         torch.cuda.synchronize()
-        step_layers, step_lm = g_layers.replay, g_lm.replay
+        step, step_layers, step_lm = g_step.replay, g_layers.replay, g_lm.replay
     else:
+        def step():
+            run_layers()
+            run_lmhead()
         step_layers, step_lm = run_layers, run_lmhead
 
     stream = torch.cuda.current_stream()
@@ -322,15 +333,23 @@ def main() -> int:
         return sorted(ts)[1]
 
     for _ in range(args.warmup):
-        step_layers()
-        step_lm()
+        step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done (graph={use_graph})")
 
+    # the timed region: exactly K steps, nothing else enqueued
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    # the layers / lm_head split of the same step, from HIP events (untimed for `value`)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         step_layers()
@@ -338,8 +357,6 @@ def main() -> int:
         step_lm()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
     layers_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
     lm_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
     med_layers_ms = layers_ms[len(layers_ms) // 2]
@@ -347,15 +364,14 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; layers {med_layers_ms:.3f} ms, "
         f"lm_head {med_lm_ms:.3f} ms (median)")
 
-    # eager launch rate of the same step, for context
+    # eager launches of the same step, same protocol, for context
     torch.cuda.synchronize()
     te = time.perf_counter()
-    n_eager = max(3, args.steps // 5)
-    for _ in range(n_eager):
+    for _ in range(args.steps):
         run_layers()
         run_lmhead()
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - te) * 1e3 / n_eager
+    eager_ms = (time.perf_counter() - te) * 1e3 / args.steps
 
     # ------------------------------------- dominant kernel: fused gate+up
     # 34 back-to-back launches (one per layer, so every launch streams its
