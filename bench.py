@@ -429,6 +429,45 @@ def main() -> int:
     lm_plain_us = time_graph(run_lmhead_plain, 10)
     log(f"lm_head top-5: {lm_plain_us:.2f} us; with probabilities: {lm_probs_us:.2f} us")
 
+    # ------------------- per configuration: us per call and GB/s of each call
+    # tiny 256x512 matvec (one matrix, latency); fused QKV rotated over 102
+    # distinct 4096x2560 Q4_K regions (the first 5.9 MB of every layer's Wg,
+    # Wu and Wd: 600 MB, beyond the 256 MB Infinity Cache); the FFN over the 34
+    # layers; lm_head top-5 and the prefill FFN as timed above.
+    per_config = None
+    if need_layers and need_lm:
+        tiny = inputs.tiny_matvec()
+        t_W, t_x, t_y = up(tiny["W"]), up(tiny["x"]), torch.empty(256, device=dev)
+        tiny_us = time_graph(lambda: q4k.q4k_matvec(t_W, t_x, t_y, 256, 512), 100)
+        qkv_w = wbytes(QROWS + 2 * KVROWS, HIDDEN)
+        qkv_regions = [L[m][:qkv_w] for L in ffn_dev for m in ("Wg", "Wu", "Wd")]
+
+        def run_qkv_rot():
+            for i, Wr in enumerate(qkv_regions):
+                q4k.q4k_qkv(Wr, qkv_dev[i % LAYERS]["x"], q, k, v, QROWS, KVROWS, HIDDEN)
+
+        def run_ffn_only():
+            for L in ffn_dev:
+                q4k.q4k_ffn(L["Wg"], L["Wu"], L["Wd"], L["x"], y, HIDDEN, INTER, GELU, h)
+
+        qkv_us = time_graph(run_qkv_rot, 1) / len(qkv_regions)
+        ffn_us = time_graph(run_ffn_only, 1) / LAYERS
+        ffn_bytes = GATE_UP_BYTES + DOWN_BYTES
+        tiny_bytes = wbytes(256, 512) + 512 * 4 + 256 * 4
+
+        def leg(us, nbytes):
+            gbs = nbytes / (us * 1e-6) / 1e9
+            return {"us_per_call": round(us, 3), "gbs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes}
+
+        per_config = {
+            "tiny_matvec_256x512": leg(tiny_us, tiny_bytes),
+            "qkv_4096x2560": leg(qkv_us, QKV_BYTES),
+            "ffn_layer_gate_up_down": leg(ffn_us, ffn_bytes),
+            "lm_head_262144x2560_top5": leg(lm_plain_us, LMHEAD_BYTES - TOPK * 4 - 4),
+        }
+        log("per config: " + ", ".join(f"{n} {d['us_per_call']:.2f} us" for n, d in per_config.items()))
+
     # ----------------------------- Q6_K matvec at the down-projection shape
     q6k_leg = None
     if do_q6k:
@@ -586,6 +625,7 @@ def main() -> int:
             "us_per_launch": round(gu_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
+        "per_config": per_config,
         "prefill": prefill,
         "q6k_matvec": q6k_leg,
         "tp8_shard": shard_leg,
