@@ -103,6 +103,22 @@ def test_matvec_wide_rows_multipass_conversion(q4k, orc, rows, cols):
     assert_close(y, ref, A, what=f"matvec {rows}x{cols}")
 
 
+# A non-finite activation reaches every output (reading C3: NaN/Inf propagate),
+# in the f32 path and in block floating point (the sub-block's scale becomes
+# NaN), whichever conversion pass the value falls in.
+@pytest.mark.parametrize("rows,cols", [(256, 2560), (16384, 2560), (8195, 10240), (5003, 16384)])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), -float("inf")])
+def test_matvec_non_finite_activation(q4k, orc, rows, cols, bad):
+    rng = np.random.default_rng(rows + cols)
+    W = inputs.q4k_random(rng, rows, cols)
+    x = inputs.normal_f32(rng, cols)
+    x[cols - 37] = bad
+    y = gpu_matvec(q4k, W, x, rows, cols)
+    ref, _ = orc.matvec(W, x, rows, cols)
+    assert not np.any(np.isfinite(ref))
+    assert not np.any(np.isfinite(y)), f"{int(np.isfinite(y).sum())} finite outputs"
+
+
 def test_matvec_crafted_fields(q4k, orc):
     """Zero nibbles, zero d, saturated fields and extreme binary16 scales."""
     rng = np.random.default_rng(21)
