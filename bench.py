@@ -113,9 +113,16 @@ def cpu_baseline(data, budget_s: float):
     oracle.softmax(y_lm)
     done_bytes += wbytes(lm_rows, HIDDEN) + HIDDEN * 4 + lm_rows * 4
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{layers} decode layers (fused QKV + gate/up/down FFN) + {lm_rows} of "
-                      f"{VOCAB} lm_head rows, single-threaded f64 C oracle, {dt:.1f} s"}
+                      f"{VOCAB} lm_head rows, single-threaded f64 C oracle, {dt:.1f} s",
+            "host": {"cpu": model, "logical_cpus": os.cpu_count()}}
 
 
 def main() -> int:
