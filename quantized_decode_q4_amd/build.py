@@ -28,10 +28,16 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, debug_sync: bool | None = None) -> str:
+    """Compile libq4k.so. debug_sync (default: environment Q4K_DEBUG_SYNC=1)
+    builds the debugging variant in which every call waits for its stream and
+    reports a kernel that failed while running as Q4K_ERR_HIP."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if debug_sync is None:
+        debug_sync = os.environ.get("Q4K_DEBUG_SYNC", "") == "1"
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
+    defs = ["-DQ4K_DEBUG_SYNC"] if debug_sync else []
+    cmd = [hipcc, *HIPCC_FLAGS, *defs, f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

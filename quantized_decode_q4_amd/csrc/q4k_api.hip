@@ -22,6 +22,20 @@ int hip_status(hipError_t e)
     return Q4K_ERR_HIP;
 }
 
+// Status of a call's launches. Built with Q4K_DEBUG_SYNC, the call also waits
+// for its stream and reports a kernel that failed while running (a debugging
+// aid: such a build cannot be captured into a graph).
+int finish(hipError_t e, hipStream_t s)
+{
+#ifdef Q4K_DEBUG_SYNC
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+#else
+    (void)s;
+#endif
+    return hip_status(e);
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Half-open byte range of a tensor; empty ranges overlap nothing.
@@ -73,8 +87,8 @@ Q4K_EXPORT int q4k_matvec(const void *W, const float *x, float *y, int64_t rows,
     const Span sy = span(y, rows * 4);
     if (overlap(sy, span(W, wbytes(rows, cols))) || overlap(sy, span(x, cols * 4)))
         return Q4K_ERR_ALIAS;
-    return hip_status(q4k::launch_rows_store((const uint8_t *)W, x, y, nullptr, nullptr, rows,
-                                             cols, rows, rows, as_stream(stream)));
+    return finish(q4k::launch_rows_store((const uint8_t *)W, x, y, nullptr, nullptr, rows,
+                                             cols, rows, rows, as_stream(stream)), as_stream(stream));
 }
 
 Q4K_EXPORT int q6k_matvec(const void *W, const float *x, float *y, int64_t rows, int64_t cols,
@@ -88,8 +102,8 @@ Q4K_EXPORT int q6k_matvec(const void *W, const float *x, float *y, int64_t rows,
     if (overlap(sy, span(W, rows * (cols / Q4K_QK) * Q6K_BLOCK_BYTES)) ||
         overlap(sy, span(x, cols * 4)))
         return Q4K_ERR_ALIAS;
-    return hip_status(q4k::launch_q6k_matvec((const uint8_t *)W, x, y, rows, cols,
-                                             as_stream(stream)));
+    return finish(q4k::launch_q6k_matvec((const uint8_t *)W, x, y, rows, cols,
+                                             as_stream(stream)), as_stream(stream));
 }
 
 Q4K_EXPORT int q4k_qkv(const void *Wqkv, const float *x, float *q, float *k, float *v,
@@ -111,8 +125,8 @@ Q4K_EXPORT int q4k_qkv(const void *Wqkv, const float *x, float *q, float *k, flo
         for (int j = i + 1; j < 3; ++j)
             if (overlap(out[i], out[j])) return Q4K_ERR_ALIAS;
     }
-    return hip_status(q4k::launch_rows_store((const uint8_t *)Wqkv, x, q, k, v, rows, cols,
-                                             q_rows, q_rows + kv_rows, as_stream(stream)));
+    return finish(q4k::launch_rows_store((const uint8_t *)Wqkv, x, q, k, v, rows, cols,
+                                             q_rows, q_rows + kv_rows, as_stream(stream)), as_stream(stream));
 }
 
 Q4K_EXPORT int q4k_gate_up(const void *Wg, const void *Wu, const float *x, float *h,
@@ -128,8 +142,8 @@ Q4K_EXPORT int q4k_gate_up(const void *Wg, const void *Wu, const float *x, float
     if (overlap(sh, span(Wg, wbytes(inter, hidden))) || overlap(sh, span(Wu, wbytes(inter, hidden))) ||
         overlap(sh, span(x, hidden * 4)))
         return Q4K_ERR_ALIAS;
-    return hip_status(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu, x, h, inter,
-                                          hidden, act, as_stream(stream)));
+    return finish(q4k::launch_gate_up((const uint8_t *)Wg, (const uint8_t *)Wu, x, h, inter,
+                                          hidden, act, as_stream(stream)), as_stream(stream));
 }
 
 Q4K_EXPORT size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter)
@@ -157,9 +171,9 @@ Q4K_EXPORT int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const flo
     if (overlap(sy, sw)) return Q4K_ERR_ALIAS;
     for (int j = 0; j < 4; ++j)
         if (overlap(sy, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
-    return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+    return finish(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                       (const uint8_t *)Wd, x, y, hidden, inter, act,
-                                      (float *)ws, as_stream(stream)));
+                                      (float *)ws, as_stream(stream)), as_stream(stream));
 }
 
 // ------------------------------------------------ fused residual RMSNorm ---
@@ -203,8 +217,8 @@ Q4K_EXPORT int q4k_rmsnorm_matvec(const void *W, const float *h, const float *de
     const int c = norm_checks(h, delta, norm_w, eps, h_out, cols, &sw, 1, &sy, 1);
     if (c != Q4K_OK) return c;
     const q4k::NormIn n = {delta, norm_w, eps, h_out};
-    return hip_status(q4k::launch_rows_store((const uint8_t *)W, h, y, nullptr, nullptr, rows,
-                                             cols, rows, rows, as_stream(stream), &n));
+    return finish(q4k::launch_rows_store((const uint8_t *)W, h, y, nullptr, nullptr, rows,
+                                             cols, rows, rows, as_stream(stream), &n), as_stream(stream));
 }
 
 Q4K_EXPORT int q4k_rmsnorm_ffn(const void *Wg, const void *Wu, const void *Wd, const float *h,
@@ -229,9 +243,9 @@ Q4K_EXPORT int q4k_rmsnorm_ffn(const void *Wg, const void *Wu, const void *Wd, c
     const int c = norm_checks(h, delta, norm_w, eps, h_out, hidden, ins, 3, outs, 2);
     if (c != Q4K_OK) return c;
     const q4k::NormIn n = {delta, norm_w, eps, h_out};
-    return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+    return finish(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                       (const uint8_t *)Wd, h, y, hidden, inter, act,
-                                      (float *)ws, as_stream(stream), &n));
+                                      (float *)ws, as_stream(stream), &n), as_stream(stream));
 }
 
 // lm_head workspace: the per-workgroup candidate lists (k keys of 8 bytes
@@ -280,10 +294,10 @@ static int lmhead_call(const void *W, const float *x, float *logits, int64_t row
     }
     uint8_t *w8 = (uint8_t *)ws;
     float2 *stats = probs ? (float2 *)(w8 + lmhead_cand_bytes(rows, cols, k)) : nullptr;
-    return hip_status(q4k::launch_lmhead_topk((const uint8_t *)W, x, logits, rows, cols, k,
+    return finish(q4k::launch_lmhead_topk((const uint8_t *)W, x, logits, rows, cols, k,
                                               (uint64_t *)ws, top_idx, top_val, stats,
                                               probs ? top_prob : nullptr, probs ? lse : nullptr,
-                                              as_stream(stream)));
+                                              as_stream(stream)), as_stream(stream));
 }
 
 Q4K_EXPORT int q4k_lmhead_topk(const void *W, const float *x, float *logits, int64_t rows,
@@ -327,14 +341,14 @@ Q4K_EXPORT int q4k_matmul(const void *W, const float *X, float *Y, int64_t rows,
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
     if (seq >= kMfmaMinSeq) {
-        return hip_status(q4k::launch_matmul_mfma((const uint8_t *)W, X, Y, rows, cols, seq,
-                                                  (uint8_t *)ws, s));
+        return finish(q4k::launch_matmul_mfma((const uint8_t *)W, X, Y, rows, cols, seq,
+                                                  (uint8_t *)ws, s), as_stream(stream));
     }
     // f32 path: the matvec of every token in one launch (grid row = token;
     // the tokens after the first read W mostly from cache).
-    return hip_status(q4k::launch_rows_store((const uint8_t *)W, X, Y, nullptr, nullptr, rows, cols,
+    return finish(q4k::launch_rows_store((const uint8_t *)W, X, Y, nullptr, nullptr, rows, cols,
                                              rows, rows, s, nullptr,
-                                             q4k::Batch{seq, cols, rows}));
+                                             q4k::Batch{seq, cols, rows}), as_stream(stream));
 }
 
 Q4K_EXPORT size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, int64_t inter)
@@ -371,12 +385,12 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
         if (overlap(sY, in[j]) || overlap(sw, in[j])) return Q4K_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
     if (seq >= kMfmaMinSeq) {
-        return hip_status(q4k::launch_ffn_prefill_mfma((const uint8_t *)Wg, (const uint8_t *)Wu,
+        return finish(q4k::launch_ffn_prefill_mfma((const uint8_t *)Wg, (const uint8_t *)Wu,
                                                        (const uint8_t *)Wd, X, Y, seq, hidden,
-                                                       inter, act, (uint8_t *)ws, s));
+                                                       inter, act, (uint8_t *)ws, s), as_stream(stream));
     }
     // f32 path: gate+up for every token in one launch, then down likewise
-    return hip_status(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+    return finish(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                       (const uint8_t *)Wd, X, Y, hidden, inter, act, (float *)ws,
-                                      s, nullptr, seq));
+                                      s, nullptr, seq), as_stream(stream));
 }

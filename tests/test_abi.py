@@ -204,3 +204,19 @@ def test_prefill_validation():
     assert L.q4k_ffn_prefill(A, B, C, D, E, 64, 256, 512, 0, F, need - 1, S) == q4k.Q4K_ERR_WORKSPACE
     assert L.q4k_ffn_prefill(A, B, C, D, E, 0, 256, 512, 0, None, 0, S) == q4k.Q4K_OK
     assert L.q4k_ffn_prefill(A, B, C, D, F + 256, 64, 256, 512, 0, F, need, S) == q4k.Q4K_ERR_ALIAS
+
+
+def test_debug_sync_variant_compiles(tmp_path):
+    """The Q4K_DEBUG_SYNC build (every call waits for its stream and reports a
+    failed kernel as Q4K_ERR_HIP) compiles: host pass of the ABI source."""
+    import os
+    import subprocess
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([hipcc, "--offload-arch=gfx950", "--cuda-host-only", "-std=c++17", "-fsyntax-only",
+                          "-DQ4K_DEBUG_SYNC", f"-I{root}/include", f"-I{root}/quantized_decode_q4_amd/csrc",
+                          f"{root}/quantized_decode_q4_amd/csrc/q4k_api.hip"],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
