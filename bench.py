@@ -475,6 +475,36 @@ def main() -> int:
         }
         log("per config: " + ", ".join(f"{n} {d['us_per_call']:.2f} us" for n, d in per_config.items()))
 
+    # ------------- HBM reference on this machine: plain device copy and read rates
+    # (torch's own kernels, 1 GiB, context for the fractions of 8 TB/s above)
+    hbm_ref = None
+    if not args.kernel_only:
+        ref_src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        ref_dst = torch.empty_like(ref_src)
+        ref_out = torch.empty((), dtype=torch.float32, device=dev)
+
+        def timed(fn, n=5):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(n):
+                a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_ev.record(stream)
+                fn()
+                b_ev.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a_ev.elapsed_time(b_ev) * 1e-3)
+            return sorted(ts)[n // 2]
+
+        nbytes = ref_src.numel() * 4
+        t_copy = timed(lambda: ref_dst.copy_(ref_src))
+        t_sum = timed(lambda: torch.sum(ref_src, dim=0, out=ref_out))
+        hbm_ref = {"copy_1gib_gbs": round(2 * nbytes / t_copy / 1e9, 1),
+                   "read_1gib_sum_gbs": round(nbytes / t_sum / 1e9, 1)}
+        del ref_src, ref_dst
+        log(f"HBM reference: copy {hbm_ref['copy_1gib_gbs']} GB/s (read + write), "
+            f"sum {hbm_ref['read_1gib_sum_gbs']} GB/s")
+
     # ----------------------------- Q6_K matvec at the down-projection shape
     q6k_leg = None
     if do_q6k:
@@ -633,6 +663,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "hbm_reference": hbm_ref,
         "prefill": prefill,
         "q6k_matvec": q6k_leg,
         "tp8_shard": shard_leg,
