@@ -112,8 +112,9 @@ namespace {
 
 enum Epi { EPI_STORE = 0, EPI_GATE_UP = 1, EPI_LOGITS = 3 };
 // How the thread holds its 64 activations:
-//  XS_LDS    block floating point, converted cooperatively by the workgroup
-//            through LDS (byte dot products)
+//  XS_LDS    block floating point, converted through LDS (byte dot
+//            products): without a fused norm each wave converts the groups its
+//            own units read, with one the whole workgroup converts together
 //  XS_THREAD block floating point, each thread converts its own 64 (rows too
 //            wide for the LDS copy)
 //  XS_F32    plain f32 in registers (f32 multiply-adds). Used where a thread
@@ -696,8 +697,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     };
 
     // ---- activation loads go out first, then the first D sweeps ----
-    // XS_LDS: this thread's first group of 8 activations (the first pass of
-    // the cooperative conversion); XS_THREAD / XS_F32: the unit's 64 floats.
+    // XS_LDS: this thread's first groups of 8 activations (the conversion
+    // passes loaded up front); XS_THREAD / XS_F32: the unit's 64 floats.
     // With a fused norm, its inputs for the first group (XS_LDS) or the first
     // two steps of the norm pass (XS_F32 staging through LDS) go out here too.
     const int ngroups = (int)(cols / 8);
