@@ -11,7 +11,8 @@ there is fp32 accumulation order, and for the FFN the bf16 rounding of H
 computed from fp32 rather than exact G and U.
 
 Shapes are chosen so that every workgroup shape of the kernel (1..8 tiles of
-16 weight rows, K split or not) and ragged rows / tokens are exercised.
+16 weight rows, K split or not), ragged rows / tokens and the largest
+reduction length (cols = 65536) are exercised.
 """
 import numpy as np
 import pytest
@@ -88,6 +89,8 @@ MATMUL_SHAPES = [
     (9700, 256, 130),
     (300, 10240, 64),
     (2560, 2560, 128),
+    (40, 65536, 64),       # the largest cols: K split 256 ways, one super-block each
+    (300, 65536, 70),      # ... 32 ways, with two token groups
 ]
 
 
@@ -196,6 +199,7 @@ FFN_SHAPES = [
     (768, 1536, 65, 0),
     (8192, 512, 64, 1),    # gate/up pair split along K (16 splits)
     (4096, 512, 130, 0),   # ... with three token groups
+    (256, 65536, 64, 0),   # down reduces over the largest cols (K split 64 ways)
 ]
 
 
