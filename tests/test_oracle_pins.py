@@ -744,6 +744,86 @@ def test_bf16_matmul_model_within_rounding_bound(orc):
     assert err.max() > 1e-6
 
 
+def _torch_bf16(a):
+    """binary64 -> binary32 -> bfloat16 -> binary64, each cast by torch."""
+    t = torch.from_numpy(np.asarray(a, dtype=np.float64))
+    return t.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _bf16_exact_fields(rng, rows, cols):
+    """Fields whose every weight is bf16-exact: d = 2^-10, dmin = 0 and
+    sc * q <= 15 * 15 < 2^8 (eight significant bits at most)."""
+    nb = cols // 256
+    return Fields(rng, rows, cols, d=np.float16(2.0 ** -10), dmin=np.float16(0.0),
+                  sc=rng.integers(0, 16, (rows, nb, 8)), mn=np.zeros((rows, nb, 8), np.int64))
+
+
+def test_bf16_matmul_model_rounds_weights_via_binary32_and_x_to_nearest_even(orc):
+    """One-hot bf16-exact activations read back single weights: each must be
+    the field value cast f64 -> f32 -> bf16 by torch. Then bf16-exact weights
+    times arbitrary f32 activations must equal W times X cast to bf16 by torch."""
+    rng = np.random.default_rng(23)
+    rows, cols = 16, 512
+    F = Fields(rng, rows, cols)
+    W = F.to_bytes()
+    wref = _torch_bf16(F.dense())                              # rows x cols
+    X = np.eye(cols, dtype=np.float32)[::7]                    # one-hot rows, bf16-exact
+    Yb, _ = orc.matmul_bf16(W, X, rows, cols)
+    assert np.array_equal(Yb, wref[:, ::7].T)
+    # the weights above really are rounded (not all bf16-exact already)
+    assert not np.array_equal(wref, F.dense())
+
+    G = _bf16_exact_fields(rng, rows, cols)
+    Xf = rng.standard_normal((3, cols)).astype(np.float32)
+    Yb, _ = orc.matmul_bf16(G.to_bytes(), Xf, rows, cols)
+    ref = _torch_bf16(Xf.astype(np.float64)) @ G.dense().T
+    A = np.abs(_torch_bf16(Xf.astype(np.float64))) @ np.abs(G.dense()).T
+    assert np.all(np.abs(Yb - ref) <= 1e-13 * A)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_bf16_ffn_model_rounds_h_once_after_the_activation(orc, act):
+    """Composition of the bf16 FFN model, pinned from outside the oracle.
+    Every weight and activation is bf16-exact, so G and U are exact sums
+    (multiples of 2^-13 far below 2^40) and the only rounding left is that of
+    H = act(G) * U. Expected: the field-level dense weights, torch's f64
+    activation, torch's bf16 cast of H, and a numpy f64 product. A model that
+    skips the rounding of H, or rounds G and U instead of H, misses by orders
+    of magnitude more than the summation-order tolerance used here."""
+    rng = np.random.default_rng(24 + act)
+    hidden, inter, seq = 512, 768, 3
+    Fg = _bf16_exact_fields(rng, inter, hidden)
+    Fu = _bf16_exact_fields(rng, inter, hidden)
+    Fd = _bf16_exact_fields(rng, hidden, inter)
+    X = (rng.integers(-64, 65, (seq, hidden)) / 8.0).astype(np.float32)   # bf16-exact
+    Yb, _ = orc.ffn_prefill_bf16(Fg.to_bytes(), Fu.to_bytes(), Fd.to_bytes(), X, hidden, inter,
+                                 act)
+
+    xg = X.astype(np.float64)
+    G = xg @ Fg.dense().T
+    U = xg @ Fu.dense().T
+    tg = torch.from_numpy(G)
+    a = (torch.nn.functional.gelu(tg, approximate="tanh") if act == 0
+         else torch.nn.functional.silu(tg)).numpy()
+    Wd = Fd.dense()
+
+    def down(h):
+        return h @ Wd.T, np.abs(h) @ np.abs(Wd).T
+
+    Y_ref, A_ref = down(_torch_bf16(a * U))
+    tol = 1e-12 * A_ref
+    assert np.all(np.abs(Yb - Y_ref) <= tol)
+
+    # the pin discriminates: each plausible slip would fail it
+    Y_noround, _ = down(a * U)
+    tgu = torch.from_numpy(_torch_bf16(G))
+    a_r = (torch.nn.functional.gelu(tgu, approximate="tanh") if act == 0
+           else torch.nn.functional.silu(tgu)).numpy()
+    Y_gu, _ = down(a_r * _torch_bf16(U))
+    for wrong in (Y_noround, Y_gu):
+        assert np.max(np.abs(wrong - Y_ref) / tol) > 1e3
+
+
 @pytest.mark.parametrize("act", [0, 1])
 def test_activation_derivative_matches_finite_differences(orc, act):
     f = orc.gelu_tanh if act == 0 else orc.silu
