@@ -76,6 +76,9 @@
 #ifndef Q4K_GATE_UP_WGS_PER_CU
 #define Q4K_GATE_UP_WGS_PER_CU 1
 #endif
+#ifndef Q4K_GATE_UP_SPLIT
+#define Q4K_GATE_UP_SPLIT 1         // gate and up rows in two wave groups (where both fit)
+#endif
 #ifndef Q4K_DOWN_D
 #define Q4K_DOWN_D 1
 #endif
@@ -105,6 +108,9 @@
 #endif
 #ifndef Q4K_LMHEAD_WGS_PER_CU
 #define Q4K_LMHEAD_WGS_PER_CU 2
+#endif
+#ifndef Q4K_LMHEAD_WIDE
+#define Q4K_LMHEAD_WIDE 1           // lm_head: one workgroup per CU, twice the rows per sweep
 #endif
 
 namespace q4k {
@@ -582,6 +588,75 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return v;
 }
 
+// Largest 32-bit value over the 64 lanes of a wave (every lane gets it):
+// DPP row rotations, then the row and half swaps (as wave_sum_mod).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0x121>(v));
+    v = max(v, dpp_u32<0x122>(v));
+    v = max(v, dpp_u32<0x124>(v));
+    v = max(v, dpp_u32<0x128>(v));
+    {
+        uint32_t x = v, y = v;
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+        v = max(x, y);
+    }
+    {
+        uint32_t x = v, y = v;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+        v = max(x, y);
+    }
+    return v;
+}
+
+// Largest 64-bit key of a wave in two 32-bit passes: the high words, then the
+// low words of the lanes whose high word is that maximum.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+    return join_u64(mh, ml);
+}
+
+// Top-k of keys held in registers by one wave: k rounds of a lane maximum and
+// a wave maximum, the lane that holds the winner clearing it (keys are unique,
+// so exactly one key is cleared per round; 0 means no candidate). Lane 0 writes
+// the winners to dst[0..k) in rank order. NC keys per lane take part.
+template <int NC>
+__device__ __forceinline__ void wave_topk_n(uint64_t *key, int k, uint64_t *dst, int lane)
+{
+    for (int round = 0; round < k; ++round) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int c = 1; c < NC; ++c) best = key[c] > best ? key[c] : best;
+        const uint64_t win = wave_max_key(best);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) key[c] = key[c] == win ? 0ull : key[c];
+        if (lane == 0) dst[round] = win;
+    }
+}
+
+// The same for the first nc (<= MAXC, wave-uniform) keys of each lane, the
+// rest being 0: the rounds run over the next power of two of nc, so their cost
+// follows the keys actually held.
+template <int MAXC>
+__device__ __forceinline__ void wave_topk(uint64_t (&key)[MAXC], int nc, int k, uint64_t *dst,
+                                          int lane)
+{
+    nc = __builtin_amdgcn_readfirstlane(nc);
+    if (nc <= 1)
+        wave_topk_n<1>(key, k, dst, lane);
+    else if (nc <= 2)
+        wave_topk_n<(MAXC < 2 ? MAXC : 2)>(key, k, dst, lane);
+    else if (nc <= 4)
+        wave_topk_n<(MAXC < 4 ? MAXC : 4)>(key, k, dst, lane);
+    else if (nc <= 8)
+        wave_topk_n<(MAXC < 8 ? MAXC : 8)>(key, k, dst, lane);
+    else
+        wave_topk_n<MAXC>(key, k, dst, lane);
+}
+
 // Workgroup-wide maximum of a key with one barrier: wave maxima go to
 // scratch[wave], which the caller alternates between two buffers from one
 // call to the next (a buffer is rewritten only after the next call's
@@ -620,12 +695,17 @@ __device__ __forceinline__ float block_sum_f32(float v, float *scratch)
 //  XS   how the activations are held (see XSrc)
 //  D    sweeps whose loads are in flight while one sweep is computed
 //  FMT  weight format (Q4_K, or Q6_K with f32 activations)
+//  NG   wave groups: 1, or 2 for the gate/up pair, where the first half of the
+//       workgroup streams the gate rows and the second half the same up rows
+//       (each thread one matrix; twice the waves per compute unit, and the
+//       busiest SIMD issues a quarter less arithmetic). Each row's partial sums
+//       are formed by the same lanes and added in the same order either way.
 // Workgroup w processes the contiguous sweeps [S*w/G, S*(w+1)/G). The
 // activation loads and the quant/header loads of the first D sweeps are
 // issued first; then every step issues sweep i+D and computes sweep i. Wave
 // partial sums go to an LDS bank; every fb sweeps one barrier publishes them
 // and threads t < fb*RPS finish those rows.
-template <int RPS, int NMAT, int EPI, int XS, int MAXT, int D, int FMT = FMT_Q4K>
+template <int RPS, int NMAT, int EPI, int XS, int MAXT, int D, int FMT = FMT_Q4K, int NG = 1>
 __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 {
     // Grid row y works on the y-th activation vector of a batch (one vector:
@@ -636,13 +716,15 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     static_assert(RPS >= 1 && RPS <= 64 && (64 % RPS) == 0, "RPS must divide 64");
     static_assert(FMT == FMT_Q4K || (XS == XS_F32 && NMAT == 1),
                   "Q6_K: f32 activations, one matrix");
+    static_assert(NG == 1 || (NG == 2 && NMAT == 2), "wave groups split a matrix pair");
+    // matrices one thread streams
+    constexpr int LM = NG == 2 ? 1 : NMAT;
     constexpr int NW = MAXT / 64;
     constexpr int FB = Q4K_ROWS_FB;
     constexpr bool kInt = XS != XS_F32;
     __shared__ float red[2][NW][FB * NMAT * RPS];
     __shared__ float lg[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
-    __shared__ uint8_t taken[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
-    __shared__ uint64_t keys_scratch[2][EPI == EPI_LOGITS ? NW : 1];
+    __shared__ uint64_t wave_lists[EPI == EPI_LOGITS ? NW : 1][EPI == EPI_LOGITS ? kTopkMax : 1];
     __shared__ float sum_scratch[EPI == EPI_LOGITS ? NW : 1];
     __shared__ float norm_scratch[NW];
     extern __shared__ uint4 xlds_v[];   // XS_LDS: planes of x (planes_bytes(cols))
@@ -651,10 +733,16 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int t = threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = blockDim.x >> 6;
+    // wave group of the thread (uniform across a wave: the group size is a
+    // multiple of 64), its thread and wave index inside the group
+    const int gsz = (int)blockDim.x / NG;
+    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(t / gsz);
+    const int tl = t - grp * gsz;
+    const int gwave = tl >> 6;
     // sweeps per reduction batch: every row of a batch needs a thread
     const int fb = min(FB, (int)(blockDim.x / RPS));
-    const int u = t / RPS;
-    const int r = t % RPS;
+    const int u = tl / RPS;
+    const int r = tl % RPS;
     const bool uact = u < a.U;
     const int b = u >> 2, g = u & 3;
     const int sh = (g & 1) * 16;
@@ -680,11 +768,11 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // below 2^30 bytes); offsets are relative to row_begin. Q6_K rows start at
     // even bytes only: the resource then begins at the 4-byte boundary below
     // (lead bytes of the previous row, never read as part of this one).
-    __amdgpu_buffer_rsrc_t rs[NMAT];
+    __amdgpu_buffer_rsrc_t rs[LM];
     uint32_t lead = 0;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        const uint8_t *base = (m == 0 ? a.W0 : a.W1) + row_begin * rowbytes;
+    for (int m = 0; m < LM; ++m) {
+        const uint8_t *base = ((m + grp) == 0 ? a.W0 : a.W1) + row_begin * rowbytes;
         if (FMT == FMT_Q6K) lead = (uint32_t)((uintptr_t)base & 3u);
         rs[m] = make_rsrc(base - lead, (uint32_t)((row_span_end - row_begin) * rowbytes) + lead);
     }
@@ -724,7 +812,10 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // takes groups t, t + blockDim, ... and a barrier publishes the planes.
     const bool wave_local = Q4K_WAVE_LOCAL_X && XS == XS_LDS && a.nw == nullptr;
     const int gpw = 512 / RPS;
-    const int gbase = wave * gpw;
+    const int gbase = gwave * gpw;
+    // activation planes in LDS: one copy per wave group when each wave converts
+    // its own (no barrier between the groups), else one shared copy
+    uint8_t *const xp = xlds + (wave_local ? (int64_t)grp * planes_bytes(cols) : 0);
     const int gpasses = wave_local ? (gpw + 63) / 64 : (ngroups + (int)blockDim.x - 1) / (int)blockDim.x;
     // group of pass i of this thread, or ngroups for none
     auto group_of = [&](int i) -> int {
@@ -785,12 +876,12 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // first sweeps of weights. A compiler barrier keeps that order.
     asm volatile("" ::: "memory");
 
-    using SlotT = std::conditional_t<FMT == FMT_Q6K, Slot6<NMAT>, Slot<NMAT>>;
+    using SlotT = std::conditional_t<FMT == FMT_Q6K, Slot6<LM>, Slot<LM>>;
     auto issue = [&](SlotT &sl, uint32_t off) {
         if constexpr (FMT == FMT_Q6K)
-            load_slot6<NMAT>(sl, rs, off, g >> 1, g & 1);
+            load_slot6<LM>(sl, rs, off, g >> 1, g & 1);
         else
-            load_slot<NMAT>(sl, rs, off, qoff);
+            load_slot<LM>(sl, rs, off, qoff);
     };
     // The first kPre sweeps go out before the activations are prepared, the
     // rest of the first D right after (a deeper early burst delays the
@@ -897,7 +988,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     } else {
         // Cooperative conversion: 4 threads per 32-activation sub-block, 8
         // activations each; max and sum over the 4 lanes of a quad (DPP).
-        float *Xs = reinterpret_cast<float *>(xlds + 3 * cols);
+        float *Xs = reinterpret_cast<float *>(xp + 3 * cols);
         float *Ss = Xs + cols / 32;
         // group e of 8 activations (x, and with a norm delta and nw, given)
         auto convert = [&](int e, uint4 h0, uint4 h1, uint4 d0, uint4 d1, uint4 w0, uint4 w1) {
@@ -947,7 +1038,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             if (e < ngroups) {
 #pragma unroll
                 for (int pl = 0; pl < 3; ++pl)
-                    *reinterpret_cast<uint2 *>(xlds + pl * cols + 8 * e) =
+                    *reinterpret_cast<uint2 *>(xp + pl * cols + 8 * e) =
                         make_uint2(p[pl][0], p[pl][1]);
                 if ((e & 3) == 0) {
                     Xs[e >> 2] = X;
@@ -994,7 +1085,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         if (uact) {
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl) {
-                const uint4 *q = reinterpret_cast<const uint4 *>(xlds + pl * cols + 64 * u);
+                const uint4 *q = reinterpret_cast<const uint4 *>(xp + pl * cols + 64 * u);
                 const uint4 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
                 xu.pa[pl][0] = v0.x; xu.pa[pl][1] = v0.y; xu.pa[pl][2] = v0.z; xu.pa[pl][3] = v0.w;
                 xu.pa[pl][4] = v1.x; xu.pa[pl][5] = v1.y; xu.pa[pl][6] = v1.z; xu.pa[pl][7] = v1.w;
@@ -1022,7 +1113,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     int kb = 0, bank = 0;
     auto compute_sweep = [&](const SlotT &sl, int64_t sj) {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
+        for (int m = 0; m < LM; ++m) {
             float v;
             if constexpr (FMT == FMT_Q6K)
                 v = unit_dot_q6(sl.q[m], sl.sc[m], sl.d[m], sl.mis, xf, s6, g & 1);
@@ -1030,7 +1121,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 v = kInt ? unit_dot(sl.q[m], sl.h[m], xu, sh, upper)
                          : unit_dot_f32(sl.q[m], sl.h[m], xf, sh, upper);
             v = wave_sum_mod<RPS>(v);
-            if (lane < RPS) red[bank][wave][(kb * NMAT + m) * RPS + lane] = v;
+            if (lane < RPS) red[bank][wave][(kb * NMAT + m + grp) * RPS + lane] = v;
         }
         ++kb;
         if (kb == fb || sj == n_loc - 1) {
@@ -1041,9 +1132,18 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 const int64_t row = gsweep(li) * RPS + rr;
                 if (row < a.rows) {
                     float v0 = 0.f, v1 = 0.f;
-                    for (int w = 0; w < nwaves; ++w) {
-                        v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
-                        if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
+                    if (NG == 1) {
+                        for (int w = 0; w < nwaves; ++w) {
+                            v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
+                            if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
+                        }
+                    } else {
+                        // gate partials from the first group's waves, up from the second's
+                        const int gw = nwaves / 2;
+                        for (int w = 0; w < gw; ++w) {
+                            v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
+                            v1 += red[bank][gw + w][(k * NMAT + 1) * RPS + rr];
+                        }
                     }
                     if (norm) {
                         v0 *= inv_rms;
@@ -1061,7 +1161,6 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                     } else {
                         a.o0[row] = v0;
                         lg[li * RPS + rr] = v0;
-                        taken[li * RPS + rr] = 0;
                     }
                 }
             }
@@ -1093,33 +1192,51 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     }
 
     if (EPI == EPI_LOGITS) {
-        // Per-workgroup top-k of its rows, written in rank order: k rounds of
-        // a workgroup-wide max over orderable keys. The thread that owns the
-        // winning row (row j is scanned by thread j mod blockDim) marks it
-        // taken, so the mark needs no barrier of its own.
+        // Per-workgroup top-k of its rows, written in rank order. Each wave
+        // takes the top-k of a contiguous slice of the rows, held as orderable
+        // keys in registers: k rounds of a lane maximum and a wave maximum, the
+        // lane holding the winner clearing it (keys are unique: they embed the
+        // row). No barrier or LDS access inside the rounds. Wave 0 then merges
+        // the waves' lists the same way.
         __syncthreads();
         // local row j = i * RPS + rr is global row gsweep(i) * RPS + rr; rows
         // past the end (a partial last sweep) are skipped
         const int n = (int)(n_loc * RPS);
         auto grow = [&](int j) -> int64_t { return gsweep(j / RPS) * RPS + j % RPS; };
         uint64_t *out = a.cand + (int64_t)blockIdx.x * a.k;
-        float wg_max = 0.f;
-        for (int round = 0; round < a.k; ++round) {
-            uint64_t best = 0;
-            for (int j = t; j < n; j += blockDim.x) {
+        // slices of at most kLmheadRowsPerWgMax / 4 rows: every launch has >= 4 waves
+        constexpr int kKeysPerLane = kLmheadRowsPerWgMax / (4 * 64);
+        const int per_wave = (n + nwaves - 1) / nwaves;
+        const int cpl = (per_wave + 63) / 64;
+        uint64_t key[kKeysPerLane];
+#pragma unroll
+        for (int c = 0; c < kKeysPerLane; ++c) {
+            const int o = c * 64 + lane;
+            const int j = wave * per_wave + o;
+            uint64_t kk = 0;
+            if (c < cpl && o < per_wave && j < n) {
                 const int64_t gr = grow(j);
-                if (gr >= a.rows || taken[j]) continue;
-                const uint64_t kk = topk_key(lg[j], (uint32_t)gr);
-                best = kk > best ? kk : best;
+                if (gr < a.rows) kk = topk_key(lg[j], (uint32_t)gr);
             }
-            const uint64_t win = block_max_u64(best, keys_scratch[round & 1]);
-            if (round == 0) wg_max = topk_key_value(win);
-            if (win != 0) {
-                const int64_t gr = (int64_t)(~(uint32_t)(win & 0xFFFFFFFFu));
-                const int j = (int)(((gr / RPS) - s_begin) / s_step * RPS + gr % RPS);
-                if (j % (int)blockDim.x == t) taken[j] = 1;
+            key[c] = kk;
+        }
+        wave_topk(key, cpl, a.k, wave_lists[wave], lane);
+        __syncthreads();
+        // the workgroup's largest logit: the largest of the waves' first winners
+        uint64_t top = 0;
+        for (int w = 0; w < nwaves; ++w) top = wave_lists[w][0] > top ? wave_lists[w][0] : top;
+        const float wg_max = topk_key_value(top);
+        if (wave == 0) {
+            constexpr int kMergePerLane = NW * kTopkMax / 64;
+            const int total = nwaves * a.k;
+            const int mpl = (total + 63) / 64;
+            uint64_t m[kMergePerLane];
+#pragma unroll
+            for (int c = 0; c < kMergePerLane; ++c) {
+                const int i = c * 64 + lane;
+                m[c] = (c < mpl && i < total) ? wave_lists[i / a.k][i % a.k] : 0ull;
             }
-            if (t == 0) out[round] = win;
+            wave_topk(m, mpl, a.k, out, lane);
         }
         if (a.stats) {
             // softmax partial of this workgroup: m = its largest logit (the
@@ -1137,18 +1254,21 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 }
 
 // Merge of the per-workgroup candidate lists (each sorted in rank order) into
-// the global top-k: a k-way merge. Thread t owns lists t, t+256, ...; each
-// round the workgroup takes the largest list head and that list advances.
-// When all lists fit, they are first copied to LDS (all loads issued at
-// once), so that advancing a list costs an LDS read instead of a dependent
-// global load.
+// the global top-k. Fast path (all candidates fit kMergeRegKeys per thread):
+// every key is loaded into registers with all loads in flight, each wave takes
+// the top-k of its share (wave_topk: no barriers) and wave 0 the top-k of the
+// four waves' lists. Otherwise a k-way merge: thread t owns lists t, t+256,
+// ...; each round the workgroup takes the largest list head and that list
+// advances (lists staged in LDS when they fit).
 // With stats, the per-workgroup softmax partials (m_w, s_w) are combined
 // against M, the largest logit (the first winner): S = sum_w s_w exp(m_w - M),
 // lse = M + log S, and a winner's probability is exp(l - M) / S.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / 64;
 constexpr int kMergeListsPerThread = 4;   // up to 1024 lists
 constexpr int kMergeStagedPerThread = 24; // 48 KB of staged candidates
 constexpr int kMergeLdsKeys = kMergeStagedPerThread * kMergeThreads;
+constexpr int kMergeRegKeys = 16;         // fast path: candidate keys per thread
 
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_t *cand, int nlists,
                                                                     int k, const float *logits,
@@ -1157,65 +1277,93 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_
                                                                     const float2 *stats,
                                                                     float *top_prob, float *lse)
 {
-    __shared__ uint64_t key_scratch[2][kMergeThreads / 64];
-    __shared__ float sum_scratch[kMergeThreads / 64];
+    __shared__ uint64_t key_scratch[2][kMergeWaves];
+    __shared__ float sum_scratch[kMergeWaves];
     __shared__ uint64_t staged[kMergeLdsKeys];
+    __shared__ uint64_t wave_wins[kMergeWaves][kTopkMax];
     __shared__ uint64_t wins[kTopkMax];
     const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     const int total = nlists * k;
-    const bool in_lds = total <= kMergeLdsKeys;
-    // the partials and the staged lists are loaded together: one memory latency
+    // the partials and the candidates are loaded together: one memory latency
     float2 st[kMergeListsPerThread];
 #pragma unroll
     for (int i = 0; i < kMergeListsPerThread; ++i) {
         const int l = t + i * kMergeThreads;
         st[i] = (stats && l < nlists) ? stats[l] : make_float2(-INFINITY, 0.f);
     }
-    if (in_lds) {
-        uint64_t v[kMergeStagedPerThread];
+    if (total <= kMergeThreads * kMergeRegKeys) {
+        const int per_wave = (total + kMergeWaves - 1) / kMergeWaves;
+        const int cpl = (per_wave + 63) / 64;
+        uint64_t key[kMergeRegKeys];
 #pragma unroll
-        for (int i = 0; i < kMergeStagedPerThread; ++i) {
-            const int j = t + i * kMergeThreads;
-            v[i] = j < total ? cand[j] : 0ull;
+        for (int c = 0; c < kMergeRegKeys; ++c) {
+            const int o = c * 64 + lane;
+            const int i = wave * per_wave + o;
+            key[c] = (c < cpl && o < per_wave && i < total) ? cand[i] : 0ull;
         }
+        wave_topk(key, cpl, k, wave_wins[wave], lane);
+        __syncthreads();
+        if (wave == 0) {
+            constexpr int kPer = kMergeWaves * kTopkMax / 64;
+            const int tot2 = kMergeWaves * k;
+            const int mpl = (tot2 + 63) / 64;
+            uint64_t m[kPer];
 #pragma unroll
-        for (int i = 0; i < kMergeStagedPerThread; ++i) {
-            const int j = t + i * kMergeThreads;
-            if (j < total) staged[j] = v[i];
+            for (int c = 0; c < kPer; ++c) {
+                const int i = c * 64 + lane;
+                m[c] = (c < mpl && i < tot2) ? wave_wins[i / k][i % k] : 0ull;
+            }
+            wave_topk(m, mpl, k, wins, lane);
         }
-    }
-    __syncthreads();
-    auto key_at = [&](int l, int pos) -> uint64_t {
-        const int i = l * k + pos;
-        return in_lds ? staged[i] : cand[i];
-    };
-    int pos[kMergeListsPerThread];
-    uint64_t head[kMergeListsPerThread];
+    } else {
+        const bool in_lds = total <= kMergeLdsKeys;
+        if (in_lds) {
+            uint64_t v[kMergeStagedPerThread];
 #pragma unroll
-    for (int i = 0; i < kMergeListsPerThread; ++i) {
-        const int l = t + i * kMergeThreads;
-        pos[i] = 0;
-        head[i] = l < nlists ? key_at(l, 0) : 0ull;
-    }
-    float M = 0.f;
-    for (int round = 0; round < k; ++round) {
-        uint64_t best = 0;
+            for (int i = 0; i < kMergeStagedPerThread; ++i) {
+                const int j = t + i * kMergeThreads;
+                v[i] = j < total ? cand[j] : 0ull;
+            }
 #pragma unroll
-        for (int i = 0; i < kMergeListsPerThread; ++i) best = head[i] > best ? head[i] : best;
-        const uint64_t win = block_max_u64(best, key_scratch[round & 1]);
-        if (round == 0) M = topk_key_value(win);
-        if (win != 0) {
-#pragma unroll
-            for (int i = 0; i < kMergeListsPerThread; ++i) {
-                if (head[i] == win) {  // keys are unique (they embed the row)
-                    const int l = t + i * kMergeThreads;
-                    ++pos[i];
-                    head[i] = pos[i] < k ? key_at(l, pos[i]) : 0ull;
-                }
+            for (int i = 0; i < kMergeStagedPerThread; ++i) {
+                const int j = t + i * kMergeThreads;
+                if (j < total) staged[j] = v[i];
             }
         }
-        if (t == 0) wins[round] = win;
+        __syncthreads();
+        auto key_at = [&](int l, int pos) -> uint64_t {
+            const int i = l * k + pos;
+            return in_lds ? staged[i] : cand[i];
+        };
+        int pos[kMergeListsPerThread];
+        uint64_t head[kMergeListsPerThread];
+#pragma unroll
+        for (int i = 0; i < kMergeListsPerThread; ++i) {
+            const int l = t + i * kMergeThreads;
+            pos[i] = 0;
+            head[i] = l < nlists ? key_at(l, 0) : 0ull;
+        }
+        for (int round = 0; round < k; ++round) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int i = 0; i < kMergeListsPerThread; ++i) best = head[i] > best ? head[i] : best;
+            const uint64_t win = block_max_u64(best, key_scratch[round & 1]);
+            if (win != 0) {
+#pragma unroll
+                for (int i = 0; i < kMergeListsPerThread; ++i) {
+                    if (head[i] == win) {  // keys are unique (they embed the row)
+                        const int l = t + i * kMergeThreads;
+                        ++pos[i];
+                        head[i] = pos[i] < k ? key_at(l, pos[i]) : 0ull;
+                    }
+                }
+            }
+            if (t == 0) wins[round] = win;
+        }
     }
+    __syncthreads();   // publishes wins[]
+    const float M = topk_key_value(wins[0]);
     const float base = M == -INFINITY ? 0.f : M;
     float S = 0.f;
     if (stats) {
@@ -1223,9 +1371,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_
 #pragma unroll
         for (int i = 0; i < kMergeListsPerThread; ++i)
             if (st[i].y != 0.f) sum += st[i].y * expf(st[i].x - base);  // NaN partials propagate
-        S = block_sum_f32(sum, sum_scratch);   // its barrier also publishes wins[]
-    } else {
-        __syncthreads();
+        S = block_sum_f32(sum, sum_scratch);
     }
     if (t < k) {
         const uint64_t win = wins[t];
@@ -1282,6 +1428,10 @@ int device_cus()
     return cache[dev];
 }
 
+// Largest workgroup of the kernels that run ten waves per compute unit in one
+// workgroup (the gate/up wave groups, the wide lm_head shape).
+constexpr int kSplitThreads = 640;
+
 template <int NMAT, int EPI, int XS, int D, int FMT = FMT_Q4K>
 hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hipStream_t s,
                        int64_t nvec = 1)
@@ -1302,8 +1452,30 @@ hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hi
     const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols)
                        : (a.nw && XS == XS_F32 && cols <= kNormLdsCols) ? (size_t)(cols * 4)
                                                                          : 0;
+    if constexpr (EPI == EPI_LOGITS && XS == XS_LDS) {
+        // the wide lm_head shape: up to ten waves in one workgroup
+        if (threads > 512 && threads <= kSplitThreads && rps > 1) {
+            switch (rps) {
+#define Q4K_RPS_CASE(R)                                                                            \
+    case R:                                                                                        \
+        hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, XS, kSplitThreads, D, FMT>), grid, block, lds, \
+                           s, a);                                                                  \
+        break;
+                Q4K_RPS_CASE(2)
+                Q4K_RPS_CASE(4)
+                Q4K_RPS_CASE(8)
+                Q4K_RPS_CASE(16)
+                Q4K_RPS_CASE(32)
+                Q4K_RPS_CASE(64)
+#undef Q4K_RPS_CASE
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     if (threads > 512) {
         // only reachable with one row per sweep (cols > 32768: no LDS planes)
+        if (rps != 1) return hipErrorInvalidValue;
         hipLaunchKernelGGL((rows_kernel<1, NMAT, EPI, XS == XS_LDS ? XS_THREAD : XS, 1024, 0, FMT>),
                            grid, block, 0, s, a);
         return hipGetLastError();
@@ -1312,6 +1484,42 @@ hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hi
 #define Q4K_RPS_CASE(R)                                                                       \
     case R:                                                                                   \
         hipLaunchKernelGGL((rows_kernel<R, NMAT, EPI, XS, 512, D, FMT>), grid, block, lds, s, a); \
+        break;
+        Q4K_RPS_CASE(1)
+        Q4K_RPS_CASE(2)
+        Q4K_RPS_CASE(4)
+        Q4K_RPS_CASE(8)
+        Q4K_RPS_CASE(16)
+        Q4K_RPS_CASE(32)
+        Q4K_RPS_CASE(64)
+#undef Q4K_RPS_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Gate/up pair in two wave groups of one workgroup (NG = 2): 2 * threads per
+// workgroup, at most kSplitThreads.
+
+template <int EPI, int XS, int D>
+hipError_t launch_rows_split(const RowsArgs &a0, int rps, int threads, int64_t nwg,
+                             hipStream_t s, int64_t nvec)
+{
+    RowsArgs a = a0;
+    const int64_t sweeps = (a.rows + rps - 1) / rps;
+    a.ilv = (Q4K_INTERLEAVE && sweeps >= kIlvMinSweeps * nwg &&
+             a.rows * (int64_t)a.nb * kBlockBytes <= ((int64_t)1 << 30))
+                ? 1
+                : 0;
+    if (nvec < 1 || nvec > 65535 || 2 * threads > kSplitThreads) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nwg, (unsigned)nvec), block((unsigned)(2 * threads));
+    const int64_t cols = (int64_t)a.nb * kQK;
+    const size_t lds = XS == XS_LDS ? (size_t)(2 * planes_bytes(cols)) : 0;
+    switch (rps) {
+#define Q4K_RPS_CASE(R)                                                                            \
+    case R:                                                                                        \
+        hipLaunchKernelGGL((rows_kernel<R, 2, EPI, XS, kSplitThreads, D, FMT_Q4K, 2>), grid, block, \
+                           lds, s, a);                                                             \
         break;
         Q4K_RPS_CASE(1)
         Q4K_RPS_CASE(2)
@@ -1425,8 +1633,15 @@ hipError_t launch_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *x, 
     a.o0 = h;
     a.act = act;
     const Shape sh = pick_shape(cols);
-    return launch_rows_bfp<2, EPI_GATE_UP, Q4K_GATE_UP_D>(
-        a, sh.rps, sh.threads, grid_for(rows, cols, sh, Q4K_GATE_UP_WGS_PER_CU), s, bt.nvec);
+    const int64_t nwg = grid_for(rows, cols, sh, Q4K_GATE_UP_WGS_PER_CU);
+    if (Q4K_GATE_UP_SPLIT && 2 * sh.threads <= kSplitThreads) {
+        if (cols <= kLdsColsMax)
+            return launch_rows_split<EPI_GATE_UP, XS_LDS, Q4K_GATE_UP_D>(a, sh.rps, sh.threads, nwg,
+                                                                         s, bt.nvec);
+        return launch_rows_split<EPI_GATE_UP, XS_THREAD, Q4K_GATE_UP_D>(a, sh.rps, sh.threads, nwg,
+                                                                        s, bt.nvec);
+    }
+    return launch_rows_bfp<2, EPI_GATE_UP, Q4K_GATE_UP_D>(a, sh.rps, sh.threads, nwg, s, bt.nvec);
 }
 
 hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, const float *x,
@@ -1461,26 +1676,47 @@ hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t
     return launch_rows<1, EPI_STORE, XS_F32, Q6K_D, FMT_Q6K>(a, sh.rps, sh.threads, nwg, s);
 }
 
-int64_t lmhead_num_wgs(int64_t rows, int64_t cols)
+// lm_head launch shape. Wide (where it fits): twice the decode shape's rows
+// per sweep in one workgroup per compute unit. Two workgroups sharing a compute
+// unit do not advance together (the older one's waves are served first: on
+// MI355X the second finished its rows ~8 us after the first, out of ~60 us), so
+// the ten waves run as one workgroup whose waves meet at every batch barrier.
+struct LmShape {
+    Shape sh;
+    int per_cu;
+};
+
+LmShape lmhead_shape(int64_t cols)
 {
     const Shape sh = pick_shape(cols);
+    if (Q4K_LMHEAD_WIDE && cols <= kLdsColsMax && 2 * sh.threads <= kSplitThreads && sh.rps <= 32)
+        return {{2 * sh.rps, 2 * sh.threads}, 1};
+    return {sh, Q4K_LMHEAD_WGS_PER_CU};
+}
+
+// Workgroups for at most g: enough that each holds at most kLmheadRowsPerWgMax
+// rows, and no more than there are sweeps.
+int64_t lmhead_grid(int64_t rows, const Shape &sh, int64_t g)
+{
     const int64_t S = (rows + sh.rps - 1) / sh.rps;
-    // enough workgroups that each holds at most kLmheadRowsPerWgMax rows
-    int64_t g = (int64_t)device_cus() * Q4K_LMHEAD_WGS_PER_CU;
-    if (g > kLmheadWgsMax) g = kLmheadWgsMax;
     const int64_t min_g = (S * sh.rps + kLmheadRowsPerWgMax - 1) / (kLmheadRowsPerWgMax - sh.rps);
     if (g < min_g) g = min_g;
     return S < g ? S : g;
 }
 
+int64_t lmhead_num_wgs(int64_t rows, int64_t cols)
+{
+    const LmShape ls = lmhead_shape(cols);
+    int64_t g = (int64_t)device_cus() * ls.per_cu;
+    if (g > kLmheadWgsMax) g = kLmheadWgsMax;
+    return lmhead_grid(rows, ls.sh, g);
+}
+
+// The same shape with the largest grid any device uses: never below
+// lmhead_num_wgs (the grid only grows with g), so it sizes the workspace.
 int64_t lmhead_max_wgs(int64_t rows, int64_t cols)
 {
-    const Shape sh = pick_shape(cols);
-    const int64_t S = (rows + sh.rps - 1) / sh.rps;
-    int64_t g = kLmheadWgsMax;
-    const int64_t min_g = (S * sh.rps + kLmheadRowsPerWgMax - 1) / (kLmheadRowsPerWgMax - sh.rps);
-    if (g < min_g) g = min_g;
-    return S < g ? S : g;
+    return lmhead_grid(rows, lmhead_shape(cols).sh, kLmheadWgsMax);
 }
 
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,
@@ -1495,7 +1731,7 @@ hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, i
     a.cand = cand;
     a.stats = stats;
     a.k = k;
-    const Shape sh = pick_shape(cols);
+    const Shape sh = lmhead_shape(cols).sh;
     const int64_t nwg = lmhead_num_wgs(rows, cols);
     hipError_t e = launch_rows_bfp<1, EPI_LOGITS, Q4K_LMHEAD_D>(a, sh.rps, sh.threads, nwg, s);
     if (e != hipSuccess) return e;
