@@ -49,6 +49,28 @@
  *  - Calls hold no global state (apart from a per-device cache of the compute
  *    unit count) and are re-entrant; calls on one stream execute in order.
  *  - Results are deterministic: no atomics, one writer per output element.
+ *
+ * Activation precision (what the arithmetic of each call is):
+ *  - f32 multiply-adds on the f32 activations: q4k_qkv, q6k_matvec, the down
+ *    projection of q4k_ffn / q4k_rmsnorm_ffn / q4k_ffn_prefill (seq < 64), and
+ *    q4k_matvec / q4k_rmsnorm_matvec / q4k_matmul (seq < 64) when a launch has
+ *    few rows per compute unit.
+ *  - Block floating point: the gate+up stage (q4k_gate_up, q4k_ffn,
+ *    q4k_rmsnorm_ffn, q4k_ffn_prefill with seq < 64), q4k_lmhead_topk(_probs),
+ *    and q4k_matvec / q4k_rmsnorm_matvec / q4k_matmul (seq < 64) with many rows
+ *    per compute unit. Each 32-activation sub-block is held as 24-bit integers
+ *    times a power of two when its largest magnitude is at most 6 times its
+ *    mean magnitude; every activation is then within 2^-22 of the sub-block's
+ *    largest magnitude (below 1.5e-6 of its mean magnitude), and the products
+ *    with the 4-bit quants are exact integer dot products. Where any sub-block
+ *    a wave covers is beyond that spread (an outlier activation), that wave
+ *    computes with f32 multiply-adds instead, so no activation is rounded at
+ *    an outlier's scale.
+ *  - bf16 operands with fp32 accumulation: q4k_matmul and q4k_ffn_prefill with
+ *    seq >= 64 (the matrix cores).
+ *  Accumulation is f32 everywhere. The weight fields enter exactly: d, dmin
+ *  (binary16), the 6-bit scales and mins and the 4-bit quants are all exact in
+ *  f32, and each sub-block contributes d*sc*sum(q x) - dmin*m*sum(x).
  */
 #ifndef Q4K_H
 #define Q4K_H
@@ -151,14 +173,22 @@ int q4k_rmsnorm_ffn(const void *Wg, const void *Wu, const void *Wd, const float 
                     int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* Largest vocabulary (rows) q4k_lmhead_topk and q4k_lmhead_topk_probs accept
+ * for this cols (0 for an invalid cols): about 4.18 million rows at cols 2560.
+ * Beyond it the calls return Q4K_ERR_SHAPE (the per-workgroup candidate lists
+ * would exceed what the merge takes). */
+int64_t q4k_lmhead_rows_max(int64_t cols);
+
 /* Workspace of q4k_lmhead_topk and q4k_lmhead_topk_probs: per-workgroup
- * top-k candidates and softmax partials. */
+ * top-k candidates and softmax partials (0 for an invalid shape or k, or rows
+ * above q4k_lmhead_rows_max(cols)). */
 size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k);
 
 /* logits = W x over all rows (the vocabulary), then the k largest logits in
  * order of value descending, index ascending (NaN logits rank last).
  * top_idx: int32[k]; top_val: f32[k] (the logits at those rows). Requires
- * 1 <= k <= min(rows, Q4K_TOPK_MAX).
+ * 1 <= k <= min(rows, Q4K_TOPK_MAX) (else Q4K_ERR_K) and
+ * rows <= q4k_lmhead_rows_max(cols) (else Q4K_ERR_SHAPE).
  * Source: Performance -- infer-inference, "Honest Path Breakdown" (GPU
  * logits) and "Real vindex" table (lm_head); infer-inference README, Overview
  * example (top-5 predictions). */
@@ -205,6 +235,27 @@ size_t q4k_ffn_prefill_workspace_bytes(int64_t seq, int64_t hidden, int64_t inte
 int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, const float *X, float *Y,
                     int64_t seq, int64_t hidden, int64_t inter, int act,
                     void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement helpers (not part of the decode path): the device-side
+ * counterparts of the pages' bandwidth and raw-dispatch profiles
+ * (infer-compute README, "Benchmarks: Profile (bottleneck analysis)").
+ *
+ * q4k_probe_read streams `bytes` bytes of the device buffer buf with the same
+ * unconditional 128-bit buffer loads as the decode kernels: `grid` workgroups
+ * of `threads` threads (a multiple of 64, at most 1024), each thread issuing
+ * `depth` loads (1, 2, 4, 8 or 16) before using their data; contiguous = 0
+ * strides the whole grid through the buffer (thread g reads the 16 bytes at
+ * (i * grid * threads + g) * 16), contiguous != 0 gives each workgroup one
+ * contiguous share. bytes: a positive multiple of 16 below 2^31; buf 16-byte
+ * aligned. sink: 4 device bytes the kernel may write (it keeps the loads from
+ * being optimised away) and that must not overlap buf.
+ * q4k_probe_empty launches a kernel with an empty body (grid x threads) into
+ * sink's stream position: the cost of one launch.
+ * Errors: Q4K_ERR_SHAPE (sizes, grid, threads, depth), Q4K_ERR_NULL,
+ * Q4K_ERR_ALIGN, Q4K_ERR_ALIAS, Q4K_ERR_HIP. */
+int q4k_probe_read(const void *buf, int64_t bytes, int grid, int threads, int depth,
+                   int contiguous, uint32_t *sink, void *stream);
+int q4k_probe_empty(int grid, int threads, uint32_t *sink, void *stream);
 
 /* Human-readable name of a q4k_status value (static string). */
 const char *q4k_status_string(int status);

@@ -255,9 +255,16 @@ static size_t lmhead_cand_bytes(int64_t rows, int64_t cols, int k)
     return round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * (size_t)k * 8, 256);
 }
 
+Q4K_EXPORT int64_t q4k_lmhead_rows_max(int64_t cols)
+{
+    if (!cols_ok(cols)) return 0;
+    return q4k::lmhead_rows_max(cols);
+}
+
 Q4K_EXPORT size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k)
 {
     if (!rows_ok(rows) || !cols_ok(cols) || rows == 0 || k < 1 || k > Q4K_TOPK_MAX) return 0;
+    if (rows > q4k::lmhead_rows_max(cols)) return 0;
     return lmhead_cand_bytes(rows, cols, k) +
            round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * 8, 256);
 }
@@ -270,7 +277,9 @@ static int lmhead_call(const void *W, const float *x, float *logits, int64_t row
 {
     if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
     if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
-    if (q4k::lmhead_max_wgs(rows, cols) > q4k::kMergeListsMax) return Q4K_ERR_SHAPE;
+    if (rows > q4k::lmhead_rows_max(cols) ||
+        q4k::lmhead_max_wgs(rows, cols) > q4k::kMergeListsMax)
+        return Q4K_ERR_SHAPE;
     if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
     if (probs && (!top_prob || !lse)) return Q4K_ERR_NULL;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||
@@ -393,4 +402,35 @@ Q4K_EXPORT int q4k_ffn_prefill(const void *Wg, const void *Wu, const void *Wd, c
     return finish(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                       (const uint8_t *)Wd, X, Y, hidden, inter, act, (float *)ws,
                                       s, nullptr, seq), as_stream(stream));
+}
+
+// ------------------------------------------------------ measurement helpers ---
+
+static bool probe_launch_ok(int grid, int threads)
+{
+    return grid >= 1 && grid <= 65536 && threads >= 64 && threads <= 1024 && threads % 64 == 0;
+}
+
+Q4K_EXPORT int q4k_probe_read(const void *buf, int64_t bytes, int grid, int threads, int depth,
+                              int contiguous, uint32_t *sink, void *stream)
+{
+    if (bytes < 16 || bytes % 16 != 0 || bytes >= ((int64_t)1 << 31) ||
+        !probe_launch_ok(grid, threads) ||
+        (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16))
+        return Q4K_ERR_SHAPE;
+    if (!buf || !sink) return Q4K_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return Q4K_ERR_ALIGN;
+    if (overlap(span(sink, 4), span(buf, bytes))) return Q4K_ERR_ALIAS;
+    return finish(q4k::launch_probe_read((const uint8_t *)buf, bytes, grid, threads, depth,
+                                         contiguous != 0, sink, as_stream(stream)),
+                  as_stream(stream));
+}
+
+Q4K_EXPORT int q4k_probe_empty(int grid, int threads, uint32_t *sink, void *stream)
+{
+    if (!probe_launch_ok(grid, threads)) return Q4K_ERR_SHAPE;
+    if (!sink) return Q4K_ERR_NULL;
+    if (!aligned(sink, 4)) return Q4K_ERR_ALIGN;
+    return finish(q4k::launch_probe_empty(grid, threads, sink, as_stream(stream)),
+                  as_stream(stream));
 }

@@ -57,6 +57,8 @@ hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t
 // any device uses for the shape (sizes the workspace).
 int64_t lmhead_num_wgs(int64_t rows, int64_t cols);
 int64_t lmhead_max_wgs(int64_t rows, int64_t cols);
+// Largest rows for which lmhead_max_wgs stays within kMergeListsMax.
+int64_t lmhead_rows_max(int64_t cols);
 // With stats (lmhead_max_wgs float2 partials), also the softmax over all
 // rows: lse[0] and top_prob[k]; stats == nullptr skips both.
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,
@@ -75,5 +77,13 @@ hipError_t launch_matmul_mfma(const uint8_t *W, const float *X, float *Y, int64_
 hipError_t launch_ffn_prefill_mfma(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd,
                                    const float *X, float *Y, int64_t seq, int64_t hidden,
                                    int64_t inter, int act, uint8_t *ws, hipStream_t s);
+
+// Measurement helpers (q4k_probe.hip): a streaming read of bytes (a multiple
+// of 16, below 2^31) at buf with 128-bit buffer loads, grid x threads, depth
+// loads in flight per thread (1, 2, 4, 8 or 16), grid-stride or one contiguous
+// range per workgroup; and an empty kernel of grid x threads.
+hipError_t launch_probe_read(const uint8_t *buf, int64_t bytes, int grid, int threads, int depth,
+                             bool contiguous, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_empty(int grid, int threads, uint32_t *sink, hipStream_t s);
 
 }  // namespace q4k

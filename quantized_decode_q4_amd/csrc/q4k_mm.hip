@@ -30,18 +30,21 @@
 //
 // Work decomposition. A workgroup owns n_t = 4A + B tiles of 16 weight rows
 // (for the gate/up pair a tile is 8 gate rows and the same 8 up rows) over a
-// range of super-blocks (a K split), for 64 tokens. Four compute waves run in
-// lockstep over the super-blocks:
-//   * tiles 0..4A-1 are "own" tiles: wave w dequantises tiles wA..wA+A-1 into
-//     its registers and multiplies them by all four token tiles;
-//   * tiles 4A..4A+B-1 are "shared": all 256 compute threads dequantise them
-//     into LDS (bf16), and wave w multiplies them by token tile w.
-// Every wave then dequantises the same number of weights and issues the same
+// range of super-blocks (a K split), for 64 tokens. Eight compute waves, two
+// per SIMD, run in lockstep over the super-blocks; the two waves of SIMD s
+// (waves s and s + 4) split every super-block's K-steps by quant-byte half, so
+// they dequantise disjoint weights and add their partial sums at the end:
+//   * tiles 0..4A-1 are "own" tiles: the pair of SIMD s dequantises tiles
+//     sA..sA+A-1 into its registers and multiplies them by all four token
+//     tiles;
+//   * tiles 4A..4A+B-1 are "shared": all 512 compute threads dequantise them
+//     into LDS (bf16), and the pair of SIMD s multiplies them by token tile s.
+// Every SIMD then dequantises the same number of weights and issues the same
 // number of MFMAs, whatever n_t is, so one workgroup per CU keeps all four
-// SIMDs equally busy. A fifth wave only copies the activation fragments of
-// the next super-blocks into an LDS ring with LDS-DMA loads; its wait counter
-// is its own, so the compute waves' weight prefetch (a register ring of
-// kRing - 1 super-blocks in flight) never waits on it.
+// SIMDs equally busy. A ninth wave only copies the activation fragments (and,
+// where they fit, the weight bytes) of the next super-blocks into LDS rings
+// with LDS-DMA loads; its wait counter is its own, so the compute waves never
+// wait on its loads except through the per-super-block barrier.
 //
 // K splits write f32 partial sums; a second kernel adds them in a fixed order
 // (and applies the gated activation for the gate/up pair). Results are

@@ -35,6 +35,12 @@
 // v_dot4_i32_i8 for p2) on the raw nibbles, exact in 32-bit integers, scaled
 // by X_s once per sub-block. The min term uses the f32 sum of the sub-block's
 // activations. Non-finite activations make X_s NaN (outputs become NaN).
+// The rounding error of an activation is below 2^-22 of its sub-block's
+// largest magnitude. A sub-block is held this way only when that magnitude is
+// at most kBfpSpread times the mean magnitude of its 32 activations, so every
+// activation is represented to within 2^-22 * 6 = 1.4e-6 of the sub-block's
+// mean magnitude. A wave whose units cover a sub-block beyond that spread (an
+// outlier activation) runs the whole launch with f32 multiply-adds instead.
 //
 // Q6_K (the other K-quant of the Shaders table, q6k_matvec; GGUF block of
 // 210 bytes: ql[128], qh[64], 16 signed scales, f16 d) runs through the same
@@ -272,6 +278,20 @@ __device__ __forceinline__ void load_slot6(Slot6<NMAT> &sl, const __amdgpu_buffe
 
 // ------------------------------------------------ block floating point ---
 
+// Largest magnitude of a sub-block held in block floating point, in units of
+// its mean magnitude (see the arithmetic note at the top).
+#ifndef Q4K_BFP_SPREAD
+#define Q4K_BFP_SPREAD 6.0f
+#endif
+constexpr float kBfpSpread = Q4K_BFP_SPREAD;
+
+// Whether 32 activations with largest magnitude amax and magnitude sum abssum
+// are within that spread (all zeros are).
+__device__ __forceinline__ bool bfp_spread_ok(float amax, float abssum)
+{
+    return 32.0f * amax <= kBfpSpread * abssum;
+}
+
 // Shift taking the sub-block to 22-bit integers and the scale back; the
 // maximum magnitude amax and the f32 sum (NaN/Inf detector) are given.
 __device__ __forceinline__ void bfp_params(float amax, float sum, int &shift, float &X)
@@ -304,31 +324,42 @@ __device__ __forceinline__ void pack4(uint32_t a, uint32_t b, uint32_t c, uint32
     P2 = __builtin_amdgcn_perm(b, a, 0x0c0c0602u) | __builtin_amdgcn_perm(d, c, 0x06020c0cu);
 }
 
-// The thread's 64 activations (sub-blocks A = 2u and B = 2u+1) as planes.
+// The thread's 64 activations (sub-blocks A = 2u and B = 2u+1), in one of two
+// forms sharing the same registers:
+//  block floating point: r[8 pl + k] is dword k of plane pl of A, r[24 + 8 pl
+//    + k] the same of B, r[48..51] = X_A, X_B, S_A, S_B (scales, f32 sums);
+//  f32 (waves outside the block-floating-point spread): r[0..31] = A,
+//    r[32..63] = B, r[64], r[65] = S_A, S_B.
 struct XUnit {
-    uint32_t pa[3][8];
-    uint32_t pb[3][8];
-    float XA, XB, SA, SB;
+    float r[66];
 };
 
-// Convert 32 f32 activations into planes (per-thread path).
-__device__ __forceinline__ void planes32(const float (&v)[32], uint32_t (&p)[3][8], float &X,
-                                         float &S)
+// Convert 32 f32 activations into planes (per-thread path): planes to
+// p[0..23] as in XUnit, scale X, sum S; false when the sub-block is beyond
+// the block-floating-point spread.
+__device__ __forceinline__ bool planes32(const float (&v)[32], float *p, float &X, float &S)
 {
-    float amax = 0.f, sum = 0.f;
+    float amax = 0.f, sum = 0.f, abssum = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         amax = fmaxf(amax, fabsf(v[i]));
         sum += v[i];
+        abssum += fabsf(v[i]);
     }
     int shift;
     bfp_params(amax, sum, shift, X);
     S = sum;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < 8; ++k) {
+        uint32_t p0, p1, p2;
         pack4((uint32_t)to_int22(v[4 * k], shift), (uint32_t)to_int22(v[4 * k + 1], shift),
               (uint32_t)to_int22(v[4 * k + 2], shift), (uint32_t)to_int22(v[4 * k + 3], shift),
-              p[0][k], p[1][k], p[2][k]);
+              p0, p1, p2);
+        p[k] = __uint_as_float(p0);
+        p[8 + k] = __uint_as_float(p1);
+        p[16 + k] = __uint_as_float(p2);
+    }
+    return bfp_spread_ok(amax, abssum);
 }
 
 // ------------------------------------------------------------ compute ---
@@ -343,12 +374,12 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&nq)[8], uint4 hd, con
     for (int k = 0; k < 8; ++k) {
         const uint32_t lo = nq[k] & 0x0F0F0F0Fu;          // sub-block A quants
         const uint32_t hi = (nq[k] >> 4) & 0x0F0F0F0Fu;   // sub-block B quants
-        a0 = __builtin_amdgcn_udot4(lo, xu.pa[0][k], a0, false);
-        a1 = __builtin_amdgcn_udot4(lo, xu.pa[1][k], a1, false);
-        a2 = __builtin_amdgcn_sdot4((int)lo, (int)xu.pa[2][k], a2, false);
-        b0 = __builtin_amdgcn_udot4(hi, xu.pb[0][k], b0, false);
-        b1 = __builtin_amdgcn_udot4(hi, xu.pb[1][k], b1, false);
-        b2 = __builtin_amdgcn_sdot4((int)hi, (int)xu.pb[2][k], b2, false);
+        a0 = __builtin_amdgcn_udot4(lo, __float_as_uint(xu.r[k]), a0, false);
+        a1 = __builtin_amdgcn_udot4(lo, __float_as_uint(xu.r[8 + k]), a1, false);
+        a2 = __builtin_amdgcn_sdot4((int)lo, (int)__float_as_uint(xu.r[16 + k]), a2, false);
+        b0 = __builtin_amdgcn_udot4(hi, __float_as_uint(xu.r[24 + k]), b0, false);
+        b1 = __builtin_amdgcn_udot4(hi, __float_as_uint(xu.r[32 + k]), b1, false);
+        b2 = __builtin_amdgcn_sdot4((int)hi, (int)__float_as_uint(xu.r[40 + k]), b2, false);
     }
     // a0 + 256 a1 < 2^25 fits in 32 bits exactly
     const float gA = fmaf(65536.0f, (float)a2, (float)(a0 + (a1 << 8)));
@@ -371,8 +402,8 @@ __device__ __forceinline__ float unit_dot(const uint32_t (&nq)[8], uint4 hd, con
     const float scB = (float)((sc2 >> 8) & 0xFFu);
     const float mA = (float)(m2 & 0xFFu);
     const float mB = (float)((m2 >> 8) & 0xFFu);
-    const float t1 = fmaf(scA * xu.XA, gA, (scB * xu.XB) * gB);
-    const float t2 = fmaf(mA, xu.SA, mB * xu.SB);
+    const float t1 = fmaf(scA * xu.r[48], gA, (scB * xu.r[49]) * gB);
+    const float t2 = fmaf(mA, xu.r[50], mB * xu.r[51]);
     return fmaf(d, t1, -dmin * t2);
 }
 
@@ -394,23 +425,25 @@ struct XF32 {
 
 // Partial dot product of one unit of one row, f32 multiply-adds. Low nibbles
 // are A's quants; high nibbles are kept in place (16q) and the factor 1/16 is
-// folded into B's scale (exact, a power of two).
-__device__ __forceinline__ float unit_dot_f32(const uint32_t (&nq)[8], uint4 hd, const XF32 &xf,
-                                              int sh, bool upper)
+// folded into B's scale (exact, a power of two). xa, xb: the 32 activations
+// of sub-blocks A and B; SA, SB their sums.
+__device__ __forceinline__ float unit_dot_f32p(const uint32_t (&nq)[8], uint4 hd, const float *xa,
+                                               const float *xb, float SA, float SB, int sh,
+                                               bool upper)
 {
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const uint32_t lo = and_opaque(nq[k], 0x0F0F0F0Fu);
         const uint32_t hi = and_opaque(nq[k], 0xF0F0F0F0u);
-        a0 = fmaf((float)(lo & 0xFFu), xf.xa[4 * k + 0], a0);
-        a1 = fmaf((float)((lo >> 8) & 0xFFu), xf.xa[4 * k + 1], a1);
-        a0 = fmaf((float)((lo >> 16) & 0xFFu), xf.xa[4 * k + 2], a0);
-        a1 = fmaf((float)(lo >> 24), xf.xa[4 * k + 3], a1);
-        b0 = fmaf((float)(hi & 0xFFu), xf.xb[4 * k + 0], b0);
-        b1 = fmaf((float)((hi >> 8) & 0xFFu), xf.xb[4 * k + 1], b1);
-        b0 = fmaf((float)((hi >> 16) & 0xFFu), xf.xb[4 * k + 2], b0);
-        b1 = fmaf((float)(hi >> 24), xf.xb[4 * k + 3], b1);
+        a0 = fmaf((float)(lo & 0xFFu), xa[4 * k + 0], a0);
+        a1 = fmaf((float)((lo >> 8) & 0xFFu), xa[4 * k + 1], a1);
+        a0 = fmaf((float)((lo >> 16) & 0xFFu), xa[4 * k + 2], a0);
+        a1 = fmaf((float)(lo >> 24), xa[4 * k + 3], a1);
+        b0 = fmaf((float)(hi & 0xFFu), xb[4 * k + 0], b0);
+        b1 = fmaf((float)((hi >> 8) & 0xFFu), xb[4 * k + 1], b1);
+        b0 = fmaf((float)((hi >> 16) & 0xFFu), xb[4 * k + 2], b0);
+        b1 = fmaf((float)(hi >> 24), xb[4 * k + 3], b1);
     }
     const float d = __half2float(__ushort_as_half((unsigned short)(hd.x & 0xFFFFu)));
     const float dmin = __half2float(__ushort_as_half((unsigned short)(hd.x >> 16)));
@@ -425,8 +458,21 @@ __device__ __forceinline__ float unit_dot_f32(const uint32_t (&nq)[8], uint4 hd,
     const float mA = (float)(m2 & 0xFFu);
     const float mB = (float)((m2 >> 8) & 0xFFu);
     const float t1 = fmaf(scA, a0 + a1, scB * (b0 + b1));
-    const float t2 = fmaf(mA, xf.SA, mB * xf.SB);
+    const float t2 = fmaf(mA, SA, mB * SB);
     return fmaf(d, t1, -dmin * t2);
+}
+
+__device__ __forceinline__ float unit_dot_f32(const uint32_t (&nq)[8], uint4 hd, const XF32 &xf,
+                                              int sh, bool upper)
+{
+    return unit_dot_f32p(nq, hd, xf.xa, xf.xb, xf.SA, xf.SB, sh, upper);
+}
+
+// The same on the f32 view of an XUnit.
+__device__ __forceinline__ float unit_dot_f32u(const uint32_t (&nq)[8], uint4 hd, const XUnit &xu,
+                                               int sh, bool upper)
+{
+    return unit_dot_f32p(nq, hd, xu.r, xu.r + 32, xu.r[64], xu.r[65], sh, upper);
 }
 
 // Q6_K partial dot product of one unit of one row, f32 multiply-adds. The
@@ -946,6 +992,9 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // ---- the thread's activations (unused units: zeros) ----
     XUnit xu;
     XF32 xf;
+    // block-floating-point launches: this wave covers a sub-block beyond the
+    // spread and computes with f32 activations (wave-uniform)
+    bool wave_f32 = false;
     float s6[4] = {0.f, 0.f, 0.f, 0.f};   // Q6_K: sums of the four quarters
     if (XS == XS_THREAD || XS == XS_F32) {
         if (z_lds) {
@@ -966,8 +1015,29 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             xf.xb[4 * i + 2] = __uint_as_float(xv[8 + i].z); xf.xb[4 * i + 3] = __uint_as_float(xv[8 + i].w);
         }
         if (XS == XS_THREAD) {
-            planes32(xf.xa, xu.pa, xu.XA, xu.SA);
-            planes32(xf.xb, xu.pb, xu.XB, xu.SB);
+            float pA[24], pB[24], XA, XB, SA, SB;
+            const bool okA = planes32(xf.xa, pA, XA, SA);
+            const bool okB = planes32(xf.xb, pB, XB, SB);
+            wave_f32 = __builtin_amdgcn_ballot_w64(uact && !(okA && okB)) != 0;
+            if (wave_f32) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    xu.r[i] = xf.xa[i];
+                    xu.r[32 + i] = xf.xb[i];
+                }
+                xu.r[64] = SA;
+                xu.r[65] = SB;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 24; ++i) {
+                    xu.r[i] = pA[i];
+                    xu.r[24 + i] = pB[i];
+                }
+                xu.r[48] = XA;
+                xu.r[49] = XB;
+                xu.r[50] = SA;
+                xu.r[51] = SB;
+            }
         } else {
             xf.SA = xf.SB = 0.f;
 #pragma unroll
@@ -1007,27 +1077,34 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                                 __uint_as_float(h0.z), __uint_as_float(h0.w),
                                 __uint_as_float(h1.x), __uint_as_float(h1.y),
                                 __uint_as_float(h1.z), __uint_as_float(h1.w)};
-            float amax = 0.f, sum = 0.f;
+            float amax = 0.f, sum = 0.f, abssum = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 amax = fmaxf(amax, fabsf(v[i]));
                 sum += v[i];
+                abssum += fabsf(v[i]);
             }
 #if Q4K_DPP_QUAD
             // quad_perm [1,0,3,2] and [2,3,0,1]: lane ^ 1, lane ^ 2
             amax = fmaxf(amax, dpp_f32<0xB1>(amax));
             sum += dpp_f32<0xB1>(sum);
+            abssum += dpp_f32<0xB1>(abssum);
             amax = fmaxf(amax, dpp_f32<0x4E>(amax));
             sum += dpp_f32<0x4E>(sum);
+            abssum += dpp_f32<0x4E>(abssum);
 #else
             amax = fmaxf(amax, __shfl_xor(amax, 1));
             sum += __shfl_xor(sum, 1);
+            abssum += __shfl_xor(abssum, 1);
             amax = fmaxf(amax, __shfl_xor(amax, 2));
             sum += __shfl_xor(sum, 2);
+            abssum += __shfl_xor(abssum, 2);
 #endif
             int shift;
             float X;
             bfp_params(amax, sum, shift, X);
+            // a negative scale marks a sub-block beyond the spread
+            if (!bfp_spread_ok(amax, abssum)) X = -1.0f;
             uint32_t p[3][2];
             pack4((uint32_t)to_int22(v[0], shift), (uint32_t)to_int22(v[1], shift),
                   (uint32_t)to_int22(v[2], shift), (uint32_t)to_int22(v[3], shift), p[0][0],
@@ -1086,22 +1163,55 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl) {
                 const uint4 *q = reinterpret_cast<const uint4 *>(xp + pl * cols + 64 * u);
-                const uint4 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
-                xu.pa[pl][0] = v0.x; xu.pa[pl][1] = v0.y; xu.pa[pl][2] = v0.z; xu.pa[pl][3] = v0.w;
-                xu.pa[pl][4] = v1.x; xu.pa[pl][5] = v1.y; xu.pa[pl][6] = v1.z; xu.pa[pl][7] = v1.w;
-                xu.pb[pl][0] = v2.x; xu.pb[pl][1] = v2.y; xu.pb[pl][2] = v2.z; xu.pb[pl][3] = v2.w;
-                xu.pb[pl][4] = v3.x; xu.pb[pl][5] = v3.y; xu.pb[pl][6] = v3.z; xu.pb[pl][7] = v3.w;
+                const uint4 qv[4] = {q[0], q[1], q[2], q[3]};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    float *dst = xu.r + (h < 2 ? 0 : 24) + 8 * pl + 4 * (h & 1);
+                    dst[0] = __uint_as_float(qv[h].x);
+                    dst[1] = __uint_as_float(qv[h].y);
+                    dst[2] = __uint_as_float(qv[h].z);
+                    dst[3] = __uint_as_float(qv[h].w);
+                }
             }
-            xu.XA = Xs[2 * u];
-            xu.XB = Xs[2 * u + 1];
-            xu.SA = Ss[2 * u];
-            xu.SB = Ss[2 * u + 1];
+            xu.r[48] = Xs[2 * u];
+            xu.r[49] = Xs[2 * u + 1];
+            xu.r[50] = Ss[2 * u];
+            xu.r[51] = Ss[2 * u + 1];
         } else {
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
+            for (int i = 0; i < 52; ++i) xu.r[i] = 0.f;
+        }
+        wave_f32 = __builtin_amdgcn_ballot_w64(uact && (xu.r[48] < 0.f || xu.r[49] < 0.f)) != 0;
+        if (wave_f32) {
+            // f32 activations of this unit, read again (with a fused norm,
+            // s * w recomputed from its inputs; the 1/rms scale is applied to
+            // the outputs as on the block-floating-point path)
+            const uint32_t xo = uact ? (uint32_t)(64 * u) * 4u : kOutOfRange;
+            uint4 fv[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xu.pa[pl][i] = xu.pb[pl][i] = 0u;
-            xu.XA = xu.XB = xu.SA = xu.SB = 0.f;
+            for (int i = 0; i < 16; ++i) fv[i] = bload16(rx, xo + 16u * i);
+            if (norm) {
+                float4 sv;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    fv[i] = norm4(fv[i], bload16(rdel, xo + 16u * i), bload16(rnw, xo + 16u * i), sv);
+            }
+            float SA = 0.f, SB = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float *dst = xu.r + 4 * i;
+                dst[0] = __uint_as_float(fv[i].x);
+                dst[1] = __uint_as_float(fv[i].y);
+                dst[2] = __uint_as_float(fv[i].z);
+                dst[3] = __uint_as_float(fv[i].w);
+            }
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                SA += xu.r[i];
+                SB += xu.r[32 + i];
+            }
+            xu.r[64] = SA;
+            xu.r[65] = SB;
         }
     }
 
@@ -1117,9 +1227,11 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             float v;
             if constexpr (FMT == FMT_Q6K)
                 v = unit_dot_q6(sl.q[m], sl.sc[m], sl.d[m], sl.mis, xf, s6, g & 1);
-            else
-                v = kInt ? unit_dot(sl.q[m], sl.h[m], xu, sh, upper)
-                         : unit_dot_f32(sl.q[m], sl.h[m], xf, sh, upper);
+            else if constexpr (!kInt)
+                v = unit_dot_f32(sl.q[m], sl.h[m], xf, sh, upper);
+            else  // wave-uniform choice: f32 activations for a wave beyond the spread
+                v = wave_f32 ? unit_dot_f32u(sl.q[m], sl.h[m], xu, sh, upper)
+                             : unit_dot(sl.q[m], sl.h[m], xu, sh, upper);
             v = wave_sum_mod<RPS>(v);
             if (lane < RPS) red[bank][wave][(kb * NMAT + m + grp) * RPS + lane] = v;
         }
@@ -1717,6 +1829,15 @@ int64_t lmhead_num_wgs(int64_t rows, int64_t cols)
 int64_t lmhead_max_wgs(int64_t rows, int64_t cols)
 {
     return lmhead_grid(rows, lmhead_shape(cols).sh, kLmheadWgsMax);
+}
+
+// lmhead_max_wgs(rows) <= kLmheadWgsMax exactly when every workgroup of that
+// grid holds at most kLmheadRowsPerWgMax - rps rows of whole sweeps, i.e. when
+// rows <= kLmheadWgsMax * (kLmheadRowsPerWgMax - rps) (a multiple of rps).
+int64_t lmhead_rows_max(int64_t cols)
+{
+    const int rps = lmhead_shape(cols).sh.rps;
+    return (int64_t)kLmheadWgsMax * (kLmheadRowsPerWgMax - rps);
 }
 
 hipError_t launch_lmhead_topk(const uint8_t *W, const float *x, float *logits, int64_t rows,

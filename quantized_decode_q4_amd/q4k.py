@@ -54,6 +54,7 @@ _SIGS = {
     "q4k_ffn_workspace_bytes": ([_I64, _I64], _SZ),
     "q4k_ffn": ([_P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P], _INT),
     "q4k_lmhead_workspace_bytes": ([_I64, _I64, _INT], _SZ),
+    "q4k_lmhead_rows_max": ([_I64], _I64),
     "q4k_lmhead_topk": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _SZ, _P], _INT),
     "q6k_matvec": ([_P, _P, _P, _I64, _I64, _P], _INT),
     "q4k_rmsnorm_matvec": ([_P, _P, _P, _P, _F32, _P, _P, _I64, _I64, _P], _INT),
@@ -64,6 +65,8 @@ _SIGS = {
     "q4k_matmul": ([_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "q4k_ffn_prefill_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q4k_ffn_prefill": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P], _INT),
+    "q4k_probe_read": ([_P, _I64, _INT, _INT, _INT, _INT, _P, _P], _INT),
+    "q4k_probe_empty": ([_INT, _INT, _P, _P], _INT),
     "q4k_status_string": ([_INT], ctypes.c_char_p),
     "q4k_last_hip_error": ([], ctypes.c_char_p),
 }
@@ -298,6 +301,20 @@ def q4k_status_string(status: int) -> str:
 
 def q4k_last_hip_error() -> str:
     return lib.q4k_last_hip_error().decode()
+
+
+def q4k_probe_read(buf, nbytes: int, grid: int, threads: int, depth: int, contiguous: bool,
+                   sink, stream=None) -> None:
+    """Streaming read of the first nbytes of buf (measurement helper)."""
+    _check(lib.q4k_probe_read(_arg(buf, "buf", nbytes), nbytes, grid, threads, depth,
+                              1 if contiguous else 0, _arg(sink, "sink", 4), _stream(stream)),
+           "q4k_probe_read")
+
+
+def q4k_probe_empty(grid: int, threads: int, sink, stream=None) -> None:
+    """An empty kernel of grid x threads (measurement helper)."""
+    _check(lib.q4k_probe_empty(grid, threads, _arg(sink, "sink", 4), _stream(stream)),
+           "q4k_probe_empty")
 
 
 def workspace(nbytes: int, device="cuda"):

@@ -75,6 +75,17 @@ int main(void)
     EXPECT(q4k_lmhead_topk(W, x, y, rows, cols, 5, ti, z, z + 64, lws - 1, S), Q4K_ERR_WORKSPACE);
     EXPECT(q4k_lmhead_topk_probs(W, x, y, rows, cols, 5, ti, z, NULL, z + 8, z + 64, lws, S),
            Q4K_ERR_NULL);
+    /* the vocabulary limit */
+    const int64_t rmax = q4k_lmhead_rows_max(cols);
+    if (rmax < 4000000 || q4k_lmhead_workspace_bytes(rmax + 1, cols, 5) != 0) fails = 1;
+    EXPECT(q4k_lmhead_topk(W, x, y, rmax + 1, cols, 5, ti, z, z + 64, (size_t)1 << 40, S),
+           Q4K_ERR_SHAPE);
+    /* measurement helpers */
+    EXPECT(q4k_probe_read(W, 0, 256, 512, 8, 0, (uint32_t *)z, S), Q4K_ERR_SHAPE);
+    EXPECT(q4k_probe_read(W, 4096, 256, 512, 3, 0, (uint32_t *)z, S), Q4K_ERR_SHAPE);
+    EXPECT(q4k_probe_read(W, 4096, 256, 512, 8, 0, NULL, S), Q4K_ERR_NULL);
+    EXPECT(q4k_probe_read(W, 4096, 256, 512, 8, 1, (uint32_t *)W, S), Q4K_ERR_ALIAS);
+    EXPECT(q4k_probe_empty(0, 256, (uint32_t *)z, S), Q4K_ERR_SHAPE);
     /* prefill */
     EXPECT(q4k_matmul(W, x, y, rows, cols, -1, z, 0, S), Q4K_ERR_SHAPE);
     EXPECT(q4k_matmul(W, x, y, rows, cols, 0, z, 0, S), Q4K_OK);

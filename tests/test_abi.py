@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "q4k_lmhead_topk_probs", "q6k_matvec", "q4k_rmsnorm_matvec", "q4k_rmsnorm_ffn",
               "q4k_matmul",
               "q4k_ffn_prefill", "q4k_status_string", "q4k_last_hip_error",
-              "q4k_ffn_workspace_bytes", "q4k_lmhead_workspace_bytes",
+              "q4k_ffn_workspace_bytes", "q4k_lmhead_workspace_bytes", "q4k_lmhead_rows_max",
               "q4k_matmul_workspace_bytes", "q4k_ffn_prefill_workspace_bytes"]:
         assert n in names
 
@@ -166,6 +166,49 @@ def test_lmhead_validation():
     assert L.q4k_lmhead_topk(A, B, C, 1000, 256, 5, D, E, C + 64, need, S) == q4k.Q4K_ERR_ALIAS
     # a vocabulary too large for the single-workgroup merge at k = 64
     assert L.q4k_lmhead_topk(A, B, C, 5_000_000, 256, 64, D, E, F, 1 << 40, S) == q4k.Q4K_ERR_SHAPE
+
+
+def test_lmhead_row_limit():
+    """The vocabulary limit the header states: rows up to q4k_lmhead_rows_max
+    size a workspace, one more is refused by the calls before any launch."""
+    L = q4k.lib
+    for cols in (256, 512, 2560, 4096, 16384, 65536):
+        rmax = L.q4k_lmhead_rows_max(cols)
+        assert rmax >= 4_000_000, (cols, rmax)
+        assert L.q4k_lmhead_workspace_bytes(rmax, cols, 5) > 0
+        assert L.q4k_lmhead_workspace_bytes(rmax + 1, cols, 5) == 0
+        assert L.q4k_lmhead_topk(A, B, C, rmax + 1, cols, 5, D, E, F, 1 << 40, S) == \
+            q4k.Q4K_ERR_SHAPE
+        assert L.q4k_lmhead_topk_probs(A, B, C, rmax + 1, cols, 5, D, E, D + 4096, E + 4096, F,
+                                       1 << 40, S) == q4k.Q4K_ERR_SHAPE
+    assert L.q4k_lmhead_rows_max(2560) == 1024 * (4096 - 16)
+    assert L.q4k_lmhead_rows_max(100) == 0 and L.q4k_lmhead_rows_max(0) == 0
+
+
+def test_probe_validation():
+    """The measurement helpers reject bad sizes, launch shapes, pointers and an
+    overlapping sink before any launch."""
+    L = q4k.lib
+    R = L.q4k_probe_read
+    assert R(A, 0, 256, 512, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4100, 256, 512, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE          # not a multiple of 16
+    assert R(A, 1 << 31, 256, 512, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4096, 0, 512, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4096, 65537, 512, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4096, 256, 500, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4096, 256, 2048, 4, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4096, 256, 512, 3, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(A, 4096, 256, 512, 32, 0, F, S) == q4k.Q4K_ERR_SHAPE
+    assert R(None, 4096, 256, 512, 4, 0, F, S) == q4k.Q4K_ERR_NULL
+    assert R(A, 4096, 256, 512, 4, 0, None, S) == q4k.Q4K_ERR_NULL
+    assert R(A + 8, 4096, 256, 512, 4, 0, F, S) == q4k.Q4K_ERR_ALIGN
+    assert R(A, 4096, 256, 512, 4, 0, F + 2, S) == q4k.Q4K_ERR_ALIGN
+    assert R(A, 4096, 256, 512, 4, 1, A + 1024, S) == q4k.Q4K_ERR_ALIAS
+    E_ = L.q4k_probe_empty
+    assert E_(0, 256, F, S) == q4k.Q4K_ERR_SHAPE
+    assert E_(256, 100, F, S) == q4k.Q4K_ERR_SHAPE
+    assert E_(256, 256, None, S) == q4k.Q4K_ERR_NULL
+    assert E_(256, 256, F + 1, S) == q4k.Q4K_ERR_ALIGN
 
 
 def test_lmhead_probs_validation():

@@ -3,6 +3,7 @@ AddressSanitizer and UndefinedBehaviorSanitizer and run through drivers under
 tests/sanitize/ (no GPU needed; every ABI call there fails a check before
 anything is enqueued). A memory error, leak (oracle) or undefined operation
 aborts the driver with a report."""
+import glob
 import os
 import shutil
 import subprocess
@@ -42,7 +43,8 @@ def test_abi_host_code_under_asan_ubsan(tmp_path):
         pytest.skip("ROCm toolchain not available")
     objs = []
     procs = []
-    for name in ("q4k_api", "q4k_rows", "q4k_mm"):
+    for name in sorted(os.path.splitext(os.path.basename(f))[0]
+                       for f in glob.glob(os.path.join(CSRC, "*.hip"))):
         obj = str(tmp_path / f"{name}.o")
         objs.append(obj)
         # sanitizers on the host pass only (the kernels are compiled as usual)
