@@ -92,7 +92,8 @@ enum q4k_status {
     Q4K_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required */
     Q4K_ERR_ALIAS = -7,     /* an output overlaps an input or another output */
     Q4K_ERR_HIP = -8,       /* a HIP runtime/launch error */
-    Q4K_ERR_EPS = -9        /* a norm's eps negative or not finite */
+    Q4K_ERR_EPS = -9,       /* a norm's eps negative or not finite */
+    Q4K_ERR_SCRATCH = -10   /* inter above Q4K_NOALLOC_INTER_MAX (q4k_ffn_noalloc) */
 };
 
 enum q4k_act {
@@ -105,6 +106,7 @@ enum q4k_act {
 #define Q6K_BLOCK_BYTES 210   /* bytes per Q6_K super-block */
 #define Q4K_TOPK_MAX 64       /* largest k of q4k_lmhead_topk */
 #define Q4K_COLS_MAX 65536    /* largest cols (reduction length) */
+#define Q4K_NOALLOC_INTER_MAX 32768  /* largest inter of q4k_ffn_noalloc (128 KB of scratch) */
 
 /* y[i] = sum_j W[i][j] * x[j], i < rows.
  * Source: infer-compute README, "Quick Start" (q4k_matvec) and "Shaders"
@@ -145,6 +147,19 @@ size_t q4k_ffn_workspace_bytes(int64_t hidden, int64_t inter);
  * followed by q4k_geglu_gelu_tanh_down / q4k_geglu_silu_down). */
 int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
             int64_t hidden, int64_t inter, int act, void *ws, size_t ws_bytes, void *stream);
+
+/* q4k_ffn for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the intermediate h
+ * lives in a scratch array inside the library instead of a caller workspace,
+ * so there is no workspace argument and the call allocates nothing. The
+ * scratch holds Q4K_NOALLOC_INTER_MAX floats per device (128 KB, kept until
+ * the process ends); a larger inter returns Q4K_ERR_SCRATCH. Every call on a
+ * device shares that device's scratch: calls that overlap on one device (on
+ * different streams, or from different threads) race and give wrong results;
+ * calls on one stream are ordered and safe. Nothing in it must start at
+ * zero. Outputs equal q4k_ffn's bit for bit (the same kernels). */
+int q4k_ffn_noalloc(const void *Wg, const void *Wu, const void *Wd, const float *x, float *y,
+                    int64_t hidden, int64_t inter, int act, void *stream);
 
 /* Residual RMSNorm fused into a projection's input (the residual_norm step
  * before a layer's projections):

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "q4k.h"
 #include "q4k_internal.h"
 
@@ -71,6 +73,7 @@ Q4K_EXPORT const char *q4k_status_string(int status)
         case Q4K_ERR_ALIAS: return "Q4K_ERR_ALIAS: an output overlaps an input or another output";
         case Q4K_ERR_HIP: return "Q4K_ERR_HIP: HIP runtime error (see q4k_last_hip_error)";
         case Q4K_ERR_EPS: return "Q4K_ERR_EPS: eps must be finite and >= 0";
+        case Q4K_ERR_SCRATCH: return "Q4K_ERR_SCRATCH: inter exceeds Q4K_NOALLOC_INTER_MAX (the no-allocation entry point's scratch)";
         default: return "unknown q4k status";
     }
 }
@@ -174,6 +177,68 @@ Q4K_EXPORT int q4k_ffn(const void *Wg, const void *Wu, const void *Wd, const flo
     return finish(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
                                       (const uint8_t *)Wd, x, y, hidden, inter, act,
                                       (float *)ws, as_stream(stream)), as_stream(stream));
+}
+
+// ------------------------------------------------- no-allocation FFN ---
+
+// The intermediate h of q4k_ffn_noalloc: a file-scope device array, so the
+// call needs no workspace and allocates nothing. Each device that runs the
+// library holds its own copy until the process ends; every call on a device
+// shares that copy (calls that overlap on one device race on it).
+static __device__ __align__(256) float scratch[Q4K_NOALLOC_INTER_MAX];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// with that device current (host code never passes the array's name itself:
+// on the host it is only a stand-in for the symbol).
+hipError_t scratch_ptr(float **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+Q4K_EXPORT int q4k_ffn_noalloc(const void *Wg, const void *Wu, const void *Wd, const float *x,
+                               float *y, int64_t hidden, int64_t inter, int act, void *stream)
+{
+    if (!cols_ok(hidden) || !cols_ok(inter)) return Q4K_ERR_SHAPE;
+    if (inter > Q4K_NOALLOC_INTER_MAX) return Q4K_ERR_SCRATCH;
+    if (act != Q4K_ACT_GELU_TANH && act != Q4K_ACT_SILU) return Q4K_ERR_ACT;
+    if (!Wg || !Wu || !Wd || !x || !y) return Q4K_ERR_NULL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(x, 16) ||
+        !aligned(y, 4))
+        return Q4K_ERR_ALIGN;
+    const Span in[4] = {span(Wg, wbytes(inter, hidden)), span(Wu, wbytes(inter, hidden)),
+                        span(Wd, wbytes(hidden, inter)), span(x, hidden * 4)};
+    const Span sy = span(y, hidden * 4);
+    for (int j = 0; j < 4; ++j)
+        if (overlap(sy, in[j])) return Q4K_ERR_ALIAS;
+    float *h = nullptr;
+    const hipError_t e = scratch_ptr(&h);
+    if (e != hipSuccess) return hip_status(e);
+    // gate+up writes all of h before the down projection reads it: nothing in
+    // the scratch needs clearing between calls
+    return finish(q4k::launch_ffn((const uint8_t *)Wg, (const uint8_t *)Wu,
+                                  (const uint8_t *)Wd, x, y, hidden, inter, act, h,
+                                  as_stream(stream)), as_stream(stream));
 }
 
 // ------------------------------------------------ fused residual RMSNorm ---

@@ -25,6 +25,8 @@ Q4K_ERR_WORKSPACE = -6
 Q4K_ERR_ALIAS = -7
 Q4K_ERR_HIP = -8
 Q4K_ERR_EPS = -9
+Q4K_ERR_SCRATCH = -10
+Q4K_NOALLOC_INTER_MAX = 32768
 Q4K_ACT_GELU_TANH = 0
 Q4K_ACT_SILU = 1
 Q4K_TOPK_MAX = 64
@@ -53,6 +55,7 @@ _SIGS = {
     "q4k_gate_up": ([_P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
     "q4k_ffn_workspace_bytes": ([_I64, _I64], _SZ),
     "q4k_ffn": ([_P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P], _INT),
+    "q4k_ffn_noalloc": ([_P, _P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
     "q4k_lmhead_workspace_bytes": ([_I64, _I64, _INT], _SZ),
     "q4k_lmhead_rows_max": ([_I64], _I64),
     "q4k_lmhead_topk": ([_P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _SZ, _P], _INT),
@@ -229,6 +232,16 @@ def q4k_ffn(Wg, Wu, Wd, x, y, hidden: int, inter: int, act: int, ws, ws_bytes: i
                        _arg(x, "x", _colv(hidden), _FLOAT), _arg(y, "y", _colv(hidden), _FLOAT),
                        hidden, inter, act, _arg(ws, "ws", ws_bytes), ws_bytes, _stream(stream)),
            "q4k_ffn")
+
+
+def q4k_ffn_noalloc(Wg, Wu, Wd, x, y, hidden: int, inter: int, act: int, stream=None) -> None:
+    """q4k_ffn without a workspace: h lives in the library's per-device scratch."""
+    _check(lib.q4k_ffn_noalloc(_arg(Wg, "Wg", _wq4(inter, hidden), _U8),
+                               _arg(Wu, "Wu", _wq4(inter, hidden), _U8),
+                               _arg(Wd, "Wd", _wq4(hidden, inter), _U8),
+                               _arg(x, "x", _colv(hidden), _FLOAT),
+                               _arg(y, "y", _colv(hidden), _FLOAT), hidden, inter, act,
+                               _stream(stream)), "q4k_ffn_noalloc")
 
 
 def q4k_lmhead_workspace_bytes(rows: int, cols: int, k: int) -> int:

@@ -106,6 +106,18 @@ def test_gate_up_and_ffn_validation():
     assert L.q4k_ffn(A, B, C, D, E, 256, 512, 0, D, need, S) == q4k.Q4K_ERR_ALIAS   # ws on x
 
 
+def test_ffn_noalloc_validation():
+    L = q4k.lib
+    F_ = L.q4k_ffn_noalloc
+    assert F_(A, B, C, D, E, 256, q4k.Q4K_NOALLOC_INTER_MAX + 256, 0, S) == q4k.Q4K_ERR_SCRATCH
+    assert F_(A, B, C, D, E, 256, 300, 0, S) == q4k.Q4K_ERR_SHAPE
+    assert F_(A, B, C, D, E, 256, 512, 7, S) == q4k.Q4K_ERR_ACT
+    assert F_(None, B, C, D, E, 256, 512, 0, S) == q4k.Q4K_ERR_NULL
+    assert F_(A + 4, B, C, D, E, 256, 512, 0, S) == q4k.Q4K_ERR_ALIGN
+    assert F_(A, B, C, D, D, 256, 512, 0, S) == q4k.Q4K_ERR_ALIAS
+    assert "Q4K_NOALLOC_INTER_MAX" in L.q4k_status_string(q4k.Q4K_ERR_SCRATCH).decode()
+
+
 def test_q6k_matvec_validation():
     P = L.q6k_matvec
     assert P(A, B, C, 10, 300, S) == q4k.Q4K_ERR_SHAPE

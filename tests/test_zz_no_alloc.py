@@ -1,0 +1,69 @@
+"""The no-allocation FFN entry point (q4k_ffn_noalloc) through the C ABI.
+
+Its intermediate h lives in the library's per-device scratch array instead of
+a caller workspace. Two calls in a row, the second on a smaller input, must
+each equal q4k_ffn on the same inputs bit for bit (the same kernels) and the
+oracle within 1e-4 A; sizes beyond the scratch are refused before any launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from quantized_decode_q4_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q4k():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_decode_q4_amd import q4k as mod
+    return mod
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def ffn_both(q4k, Wg, Wu, Wd, x, hidden, inter, act):
+    y_ref = torch.full((hidden,), float("nan"), device="cuda")
+    ws = q4k.workspace(q4k.q4k_ffn_workspace_bytes(hidden, inter))
+    q4k.q4k_ffn(Wg, Wu, Wd, x, y_ref, hidden, inter, act, ws)
+    y = torch.full((hidden,), float("nan"), device="cuda")
+    q4k.q4k_ffn_noalloc(Wg, Wu, Wd, x, y, hidden, inter, act)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), y_ref.cpu().numpy()
+
+
+def test_noalloc_ffn_two_calls_second_smaller(q4k, orc):
+    cases = [(2560, 10240, 0, None), (512, 1280, 1, 7)]   # the Gemma layer, then a smaller one
+    for hidden, inter, act, seed in cases:
+        print(f"ffn_noalloc hidden={hidden} inter={inter} act={act}", flush=True)
+        if seed is None:
+            L = inputs.ffn_layer(0)
+            Wg, Wu, Wd, x = L["Wg"], L["Wu"], L["Wd"], L["x"]
+        else:
+            rng = np.random.default_rng(seed)
+            Wg = inputs.q4k_random(rng, inter, hidden)
+            Wu = inputs.q4k_random(rng, inter, hidden)
+            Wd = inputs.q4k_random(rng, hidden, inter)
+            x = inputs.normal_f32(rng, hidden)
+        y, y_ref = ffn_both(q4k, dev(Wg), dev(Wu), dev(Wd), dev(x), hidden, inter, act)
+        assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+        r = orc.ffn(Wg, Wu, Wd, x, hidden, inter, act)
+        err = np.abs(y.astype(np.float64) - r["y"]) / r["A"]
+        print(f"  max |err|/A = {err.max():.3e}", flush=True)
+        assert err.max() <= 1e-4
+
+
+def test_noalloc_ffn_refuses_inter_beyond_the_scratch(q4k):
+    hidden, inter = 256, q4k.Q4K_NOALLOC_INTER_MAX + 256
+    W = torch.zeros(inter * 144, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(hidden, device="cuda")
+    y = torch.full((hidden,), 7.0, device="cuda")
+    st = q4k.lib.q4k_ffn_noalloc(W.data_ptr(), W.data_ptr(), W.data_ptr(), x.data_ptr(),
+                                 y.data_ptr(), hidden, inter, 0, None)
+    assert st == q4k.Q4K_ERR_SCRATCH
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
