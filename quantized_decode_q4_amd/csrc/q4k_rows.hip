@@ -103,6 +103,9 @@
 #ifndef Q4K_DPP_QUAD
 #define Q4K_DPP_QUAD 1              // quad max/sum of the conversion with DPP instead of LDS permutes
 #endif
+#ifndef Q4K_F32_X_LDS
+#define Q4K_F32_X_LDS 0             // f32 activations: one coalesced copy per workgroup in LDS
+#endif
 #ifndef Q6K_D
 #define Q6K_D 1                     // sweeps in flight, Q6_K matvec
 #endif
@@ -117,6 +120,12 @@
 #endif
 #ifndef Q4K_LMHEAD_WIDE
 #define Q4K_LMHEAD_WIDE 1           // lm_head: one workgroup per CU, twice the rows per sweep
+#endif
+#ifndef Q4K_STORE_WIDE
+#define Q4K_STORE_WIDE 0            // matvec / QKV: the same wide shape
+#endif
+#ifndef Q4K_DOWN_WIDE
+#define Q4K_DOWN_WIDE 0             // FFN down projection: the same wide shape
 #endif
 
 namespace q4k {
@@ -139,6 +148,10 @@ constexpr int kQ6Bytes = 210;   // bytes per Q6_K super-block
 // Rows up to this many columns stage the normalised activations in LDS when a
 // norm is fused into an f32-activation launch (cols * 4 bytes).
 constexpr int64_t kNormLdsCols = 8192;
+// f32-activation launches without a norm stage the activation row in LDS up to
+// this many columns (cols * 4 bytes), kXLdsLoads 16-byte loads per thread at once.
+constexpr int64_t kXLdsCols = 16384;
+constexpr int kXLdsLoads = 8;
 // Sweeps per workgroup from which a launch interleaves its sweeps.
 constexpr int64_t kIlvMinSweeps = 8;
 
@@ -167,13 +180,31 @@ struct RowsArgs {
     int32_t U;
     int32_t act;
     int32_t k;
-    int32_t chunk;           // sweeps per unit of the workgroup split
+    // Sweeps per workgroup, set by the launch: sq each, and one more for the
+    // first srem workgroups (sq * gridDim.x + srem sweeps in all).
+    int32_t sq;
+    int32_t srem;
+    int32_t nwg;             // gridDim.x
+    int32_t nthr;            // blockDim.x
     int32_t ilv;             // 1: workgroup w takes sweeps w, w+G, w+2G, ... (else a contiguous range)
     // Several activation vectors in one launch (grid row y = vector y): x
     // and o0 advance by these many floats per vector (o1, o2 unused then).
     int64_t x_stride;
     int64_t o_stride;
 };
+
+// Every kernel argument in scalar registers at once, at the top of the
+// kernel: the compiler otherwise loads each field where a branch first needs
+// it, and each such load is another memory round trip (the argument block of
+// a launch is cold) ahead of the first weight load.
+__device__ __forceinline__ void args_to_sgprs(const RowsArgs &a)
+{
+    asm volatile("" ::"s"(a.W0), "s"(a.W1), "s"(a.x), "s"(a.o0), "s"(a.o1), "s"(a.o2),
+                 "s"(a.cand), "s"(a.stats), "s"(a.delta), "s"(a.nw), "s"(a.h_out), "s"(a.eps),
+                 "s"(a.rows), "s"(a.split0), "s"(a.split1), "s"(a.nb), "s"(a.U), "s"(a.act),
+                 "s"(a.k), "s"(a.sq), "s"(a.srem), "s"(a.nwg), "s"(a.nthr), "s"(a.ilv),
+                 "s"(a.x_stride), "s"(a.o_stride));
+}
 
 __device__ __forceinline__ float act_apply(float z, int act)
 {
@@ -719,12 +750,12 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
     return m;
 }
 
-// Workgroup-wide sum with one barrier (fixed order: deterministic).
-__device__ __forceinline__ float block_sum_f32(float v, float *scratch)
+// Workgroup-wide sum over nwaves waves with one barrier (fixed order:
+// deterministic).
+__device__ __forceinline__ float block_sum_f32(float v, float *scratch, int nwaves)
 {
     v = wave_sum_mod<1>(v);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nwaves = (blockDim.x + 63) >> 6;
     if (lane == 0) scratch[wave] = v;
     __syncthreads();
     float r = scratch[0];
@@ -746,7 +777,8 @@ __device__ __forceinline__ float block_sum_f32(float v, float *scratch)
 //       (each thread one matrix; twice the waves per compute unit, and the
 //       busiest SIMD issues a quarter less arithmetic). Each row's partial sums
 //       are formed by the same lanes and added in the same order either way.
-// Workgroup w processes the contiguous sweeps [S*w/G, S*(w+1)/G). The
+// Workgroup w processes the contiguous sweeps from w*sq + min(w, srem), sq of
+// them plus one for w < srem (or, interleaved, w, w+G, ...). The
 // activation loads and the quant/header loads of the first D sweeps are
 // issued first; then every step issues sweep i+D and computes sweep i. Wave
 // partial sums go to an LDS bank; every fb sweeps one barrier publishes them
@@ -757,6 +789,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // Grid row y works on the y-th activation vector of a batch (one vector:
     // y = 0). The rows a workgroup streams depend only on blockIdx.x, so the
     // vectors after the first read the same rows, mostly from cache.
+    args_to_sgprs(a);
     a.x += (int64_t)blockIdx.y * a.x_stride;
     a.o0 += (int64_t)blockIdx.y * a.o_stride;
     static_assert(RPS >= 1 && RPS <= 64 && (64 % RPS) == 0, "RPS must divide 64");
@@ -777,16 +810,17 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     uint8_t *const xlds = reinterpret_cast<uint8_t *>(xlds_v);
 
     const int t = threadIdx.x;
+    const int nthr = a.nthr;   // blockDim.x
     const int wave = t >> 6, lane = t & 63;
-    const int nwaves = blockDim.x >> 6;
+    const int nwaves = nthr >> 6;
     // wave group of the thread (uniform across a wave: the group size is a
     // multiple of 64), its thread and wave index inside the group
-    const int gsz = (int)blockDim.x / NG;
+    const int gsz = nthr / NG;
     const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(t / gsz);
     const int tl = t - grp * gsz;
     const int gwave = tl >> 6;
     // sweeps per reduction batch: every row of a batch needs a thread
-    const int fb = min(FB, (int)(blockDim.x / RPS));
+    const int fb = min(FB, (nthr / RPS));
     const int u = tl / RPS;
     const int r = tl % RPS;
     const bool uact = u < a.U;
@@ -796,14 +830,15 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int64_t cols = (int64_t)a.nb * kQK;
     const int64_t rowbytes = (int64_t)a.nb * fmt_block_bytes(FMT);
     const int64_t unit_off = (int64_t)b * fmt_block_bytes(FMT);
-    const int64_t S = (a.rows + RPS - 1) / RPS;
     // The workgroup's sweeps, by local index i = 0 .. n_loc-1: either the
     // contiguous range [s_begin, s_end), or (ilv) sweeps w, w+G, w+2G, ... so
     // that all workgroups move through the matrix together.
     const bool ilv = a.ilv != 0;
-    const int64_t G = gridDim.x, wg = blockIdx.x;
-    const int64_t s_begin = ilv ? wg : S * wg / G;
-    const int64_t n_loc = ilv ? (S > wg ? (S - wg + G - 1) / G : 0) : S * (wg + 1) / G - s_begin;
+    // (The split comes from the host: a 64-bit division here costs hundreds
+    // of instructions ahead of the first load.)
+    const int64_t G = a.nwg, wg = blockIdx.x;
+    const int64_t n_loc = a.sq + (wg < a.srem ? 1 : 0);
+    const int64_t s_begin = ilv ? wg : wg * a.sq + (wg < a.srem ? wg : (int64_t)a.srem);
     const int64_t s_step = ilv ? G : 1;
     auto gsweep = [&](int64_t i) -> int64_t { return s_begin + i * s_step; };
     // first row the resource starts at; rows of this workgroup: [row_begin, row_span_end)
@@ -840,6 +875,11 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(cols * 4));
     const bool norm = a.nw != nullptr;
     const bool z_lds = norm && XS == XS_F32 && cols <= kNormLdsCols;
+    // Without a norm, f32 activations are read once per workgroup with
+    // coalesced loads into LDS (each thread then takes its unit's 64 from
+    // there) instead of once per thread: the RPS threads of a unit would
+    // otherwise each fetch the same 256 bytes.
+    const bool x_lds = Q4K_F32_X_LDS && !norm && XS == XS_F32 && cols <= kXLdsCols;
     const __amdgpu_buffer_rsrc_t rdel = make_rsrc(a.delta, a.delta ? (uint32_t)(cols * 4) : 0u);
     const __amdgpu_buffer_rsrc_t rnw = make_rsrc(a.nw, norm ? (uint32_t)(cols * 4) : 0u);
     // XS_LDS without a norm: the activations of the first kXPre conversion
@@ -862,14 +902,14 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // activation planes in LDS: one copy per wave group when each wave converts
     // its own (no barrier between the groups), else one shared copy
     uint8_t *const xp = xlds + (wave_local ? (int64_t)grp * planes_bytes(cols) : 0);
-    const int gpasses = wave_local ? (gpw + 63) / 64 : (ngroups + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int gpasses = wave_local ? (gpw + 63) / 64 : (ngroups + nthr - 1) / nthr;
     // group of pass i of this thread, or ngroups for none
     auto group_of = [&](int i) -> int {
         if (wave_local) {
             const int l = lane + 64 * i;
             return (l < gpw && gbase + l < ngroups) ? gbase + l : ngroups;
         }
-        const int e = t + i * (int)blockDim.x;
+        const int e = t + i * nthr;
         return e < ngroups ? e : ngroups;
     };
     if (XS == XS_LDS) {
@@ -903,10 +943,16 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) xoff[i] = xo + 16u * i;
         }
-        if (z_lds) {
+        if (x_lds) {
+#pragma unroll
+            for (int k = 0; k < kXLdsLoads; ++k) {
+                const int i = t + k * nthr;
+                xv[k] = bload16(rx, i < n4 ? (uint32_t)i * 16u : kOutOfRange);
+            }
+        } else if (z_lds) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int i = t + k * (int)blockDim.x;
+                const int i = t + k * nthr;
                 const uint32_t off = i < n4 ? (uint32_t)i * 16u : kOutOfRange;
                 nv[3 * k] = bload16(rx, off);
                 nv[3 * k + 1] = bload16(rdel, off);
@@ -978,14 +1024,14 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         int i0 = t;
         if (z_lds) {   // the first two steps were loaded with x
             if (t < n4) pass_step(t, nv[0], nv[1], nv[2]);
-            if (t + (int)blockDim.x < n4) pass_step(t + blockDim.x, nv[3], nv[4], nv[5]);
-            i0 = t + 2 * (int)blockDim.x;
+            if (t + nthr < n4) pass_step(t + nthr, nv[3], nv[4], nv[5]);
+            i0 = t + 2 * nthr;
         }
-        for (int i = i0; i < n4; i += blockDim.x) {
+        for (int i = i0; i < n4; i += nthr) {
             const uint32_t off = (uint32_t)i * 16u;
             pass_step(i, bload16(rx, off), bload16(rdel, off), bload16(rnw, off));
         }
-        const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes zl
+        const float ss = block_sum_f32(ss_part, norm_scratch, nwaves);   // also publishes zl
         inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
     }
 
@@ -997,7 +1043,18 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     bool wave_f32 = false;
     float s6[4] = {0.f, 0.f, 0.f, 0.f};   // Q6_K: sums of the four quarters
     if (XS == XS_THREAD || XS == XS_F32) {
-        if (z_lds) {
+        if (x_lds) {
+            uint4 *const xl4 = reinterpret_cast<uint4 *>(xlds);
+#pragma unroll
+            for (int k = 0; k < kXLdsLoads; ++k) {
+                const int i = t + k * nthr;
+                if (i < n4) xl4[i] = xv[k];
+            }
+            for (int i = t + kXLdsLoads * nthr; i < n4; i += nthr)
+                xl4[i] = bload16(rx, (uint32_t)i * 16u);
+            __syncthreads();
+        }
+        if (z_lds || x_lds) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 xv[i] = uact ? *reinterpret_cast<const uint4 *>(xlds + xoff[i]) : make_uint4(0, 0, 0, 0);
@@ -1148,7 +1205,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             convert(e, h0, h1, d0, d1, w0, w1);
         }
         if (norm) {
-            const float ss = block_sum_f32(ss_part, norm_scratch);   // also publishes the planes
+            const float ss = block_sum_f32(ss_part, norm_scratch, nwaves);   // also publishes the planes
             inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
         } else if (wave_local) {
             // the wave reads back only what it wrote: keep the compiler from
@@ -1357,9 +1414,9 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             // rows add 0 and NaN rows poison the sum.
             const float base = wg_max == -INFINITY ? 0.f : wg_max;
             float sum = 0.f;
-            for (int j = t; j < n; j += blockDim.x)
+            for (int j = t; j < n; j += nthr)
                 if (grow(j) < a.rows) sum += expf(lg[j] - base);
-            sum = block_sum_f32(sum, sum_scratch);
+            sum = block_sum_f32(sum, sum_scratch, nwaves);
             if (t == 0) a.stats[blockIdx.x] = make_float2(wg_max, sum);
         }
     }
@@ -1483,7 +1540,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_
 #pragma unroll
         for (int i = 0; i < kMergeListsPerThread; ++i)
             if (st[i].y != 0.f) sum += st[i].y * expf(st[i].x - base);  // NaN partials propagate
-        S = block_sum_f32(sum, sum_scratch);
+        S = block_sum_f32(sum, sum_scratch, kMergeWaves);
     }
     if (t < k) {
         const uint64_t win = wins[t];
@@ -1544,6 +1601,26 @@ int device_cus()
 // workgroup (the gate/up wave groups, the wide lm_head shape).
 constexpr int kSplitThreads = 640;
 
+// The wide shape of a launch: twice the rows per sweep, up to ten waves in
+// one workgroup, where that fits.
+Shape widen(const Shape &sh, bool on)
+{
+    if (on && 2 * sh.threads <= kSplitThreads && sh.rps <= 32) return {2 * sh.rps, 2 * sh.threads};
+    return sh;
+}
+
+// Launch geometry in the arguments: nwg workgroups of nthr threads over
+// `sweeps` sweeps, sq per workgroup and one more for the first srem.
+bool set_launch(RowsArgs &a, int64_t sweeps, int64_t nwg, int nthr)
+{
+    if (nwg < 1 || nwg > 0x7fffffff || sweeps < 0 || sweeps > 0x7fffffff) return false;
+    a.sq = (int32_t)(sweeps / nwg);
+    a.srem = (int32_t)(sweeps % nwg);
+    a.nwg = (int32_t)nwg;
+    a.nthr = nthr;
+    return true;
+}
+
 template <int NMAT, int EPI, int XS, int D, int FMT = FMT_Q4K>
 hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hipStream_t s,
                        int64_t nvec = 1)
@@ -1558,14 +1635,18 @@ hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hi
              a.rows * (int64_t)a.nb * fmt_block_bytes(FMT) <= ((int64_t)1 << 30))
                 ? 1
                 : 0;
-    if (nvec < 1 || nvec > 65535) return hipErrorInvalidValue;
+    if (nvec < 1 || nvec > 65535 || !set_launch(a, sweeps, nwg, threads))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)nwg, (unsigned)nvec), block((unsigned)threads);
     const int64_t cols = (int64_t)a.nb * kQK;
     const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols)
                        : (a.nw && XS == XS_F32 && cols <= kNormLdsCols) ? (size_t)(cols * 4)
+                       : (Q4K_F32_X_LDS && !a.nw && XS == XS_F32 && cols <= kXLdsCols)
+                           ? (size_t)(cols * 4)
                                                                          : 0;
-    if constexpr (EPI == EPI_LOGITS && XS == XS_LDS) {
-        // the wide lm_head shape: up to ten waves in one workgroup
+    if constexpr ((EPI == EPI_LOGITS && XS == XS_LDS) ||
+                  (EPI == EPI_STORE && NMAT == 1 && FMT == FMT_Q4K)) {
+        // the wide shape: up to ten waves in one workgroup
         if (threads > 512 && threads <= kSplitThreads && rps > 1) {
             switch (rps) {
 #define Q4K_RPS_CASE(R)                                                                            \
@@ -1623,7 +1704,9 @@ hipError_t launch_rows_split(const RowsArgs &a0, int rps, int threads, int64_t n
              a.rows * (int64_t)a.nb * kBlockBytes <= ((int64_t)1 << 30))
                 ? 1
                 : 0;
-    if (nvec < 1 || nvec > 65535 || 2 * threads > kSplitThreads) return hipErrorInvalidValue;
+    if (nvec < 1 || nvec > 65535 || 2 * threads > kSplitThreads ||
+        !set_launch(a, sweeps, nwg, 2 * threads))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)nwg, (unsigned)nvec), block((unsigned)(2 * threads));
     const int64_t cols = (int64_t)a.nb * kQK;
     const size_t lds = XS == XS_LDS ? (size_t)(2 * planes_bytes(cols)) : 0;
@@ -1713,7 +1796,7 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     a.o2 = o2;
     a.split0 = split0;
     a.split1 = split1;
-    const Shape sh = pick_shape(cols);
+    const Shape sh = widen(pick_shape(cols), Q4K_STORE_WIDE);
     const int64_t nwg = grid_for(rows, cols, sh, Q4K_STORE_WGS_PER_CU);
 #if Q4K_STORE_F32_SWEEPS > 0
     // few sweeps per workgroup: f32 activations, no shared conversion step.
@@ -1771,7 +1854,7 @@ hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, c
     b.o0 = y;
     b.x_stride = inter;
     b.o_stride = hidden;
-    const Shape sd = pick_shape(inter);
+    const Shape sd = widen(pick_shape(inter), Q4K_DOWN_WIDE);
     return launch_rows<1, EPI_STORE, XS_F32, Q4K_DOWN_D>(
         b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s, nvec);
 }
