@@ -103,9 +103,6 @@
 #ifndef Q4K_DPP_QUAD
 #define Q4K_DPP_QUAD 1              // quad max/sum of the conversion with DPP instead of LDS permutes
 #endif
-#ifndef Q4K_F32_X_LDS
-#define Q4K_F32_X_LDS 0             // f32 activations: one coalesced copy per workgroup in LDS
-#endif
 #ifndef Q6K_D
 #define Q6K_D 1                     // sweeps in flight, Q6_K matvec
 #endif
@@ -120,12 +117,6 @@
 #endif
 #ifndef Q4K_LMHEAD_WIDE
 #define Q4K_LMHEAD_WIDE 1           // lm_head: one workgroup per CU, twice the rows per sweep
-#endif
-#ifndef Q4K_STORE_WIDE
-#define Q4K_STORE_WIDE 0            // matvec / QKV: the same wide shape
-#endif
-#ifndef Q4K_DOWN_WIDE
-#define Q4K_DOWN_WIDE 0             // FFN down projection: the same wide shape
 #endif
 
 namespace q4k {
@@ -146,12 +137,8 @@ enum XSrc { XS_LDS = 0, XS_THREAD = 1, XS_F32 = 3 };
 enum Fmt { FMT_Q4K = 0, FMT_Q6K = 1 };
 constexpr int kQ6Bytes = 210;   // bytes per Q6_K super-block
 // Rows up to this many columns stage the normalised activations in LDS when a
-// norm is fused into an f32-activation launch (cols * 4 bytes).
+// norm is fused into an f32-activation launch (cols * 4 bytes and the padding).
 constexpr int64_t kNormLdsCols = 8192;
-// f32-activation launches without a norm stage the activation row in LDS up to
-// this many columns (cols * 4 bytes), kXLdsLoads 16-byte loads per thread at once.
-constexpr int64_t kXLdsCols = 16384;
-constexpr int kXLdsLoads = 8;
 // Sweeps per workgroup from which a launch interleaves its sweeps.
 constexpr int64_t kIlvMinSweeps = 8;
 
@@ -205,6 +192,15 @@ __device__ __forceinline__ void args_to_sgprs(const RowsArgs &a)
                  "s"(a.k), "s"(a.sq), "s"(a.srem), "s"(a.nwg), "s"(a.nthr), "s"(a.ilv),
                  "s"(a.x_stride), "s"(a.o_stride));
 }
+
+// Slot of 16-byte chunk i of an f32 activation row staged in LDS. A unit's 64
+// activations are 16 chunks (256 bytes, one pass over the LDS banks), and the
+// threads of a wave read chunk c of consecutive units together: each unit is
+// followed by one chunk of padding, so that those reads fall on different
+// banks instead of all on the same four (a 32-way conflict for two rows per
+// sweep). Unit u then starts at slot 17u.
+__device__ __forceinline__ int xslot(int i) { return i + (i >> 4); }
+constexpr int64_t kXPadNum = 17, kXPadDen = 16;   // padded size: cols * 4 * 17 / 16 bytes
 
 __device__ __forceinline__ float act_apply(float z, int act)
 {
@@ -874,12 +870,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     const int n4 = (int)(cols / 4);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(cols * 4));
     const bool norm = a.nw != nullptr;
-    const bool z_lds = norm && XS == XS_F32 && cols <= kNormLdsCols;
-    // Without a norm, f32 activations are read once per workgroup with
-    // coalesced loads into LDS (each thread then takes its unit's 64 from
-    // there) instead of once per thread: the RPS threads of a unit would
-    // otherwise each fetch the same 256 bytes.
-    const bool x_lds = Q4K_F32_X_LDS && !norm && XS == XS_F32 && cols <= kXLdsCols;
+    const bool z_lds = norm && XS == XS_F32 && FMT == FMT_Q4K && cols <= kNormLdsCols;
     const __amdgpu_buffer_rsrc_t rdel = make_rsrc(a.delta, a.delta ? (uint32_t)(cols * 4) : 0u);
     const __amdgpu_buffer_rsrc_t rnw = make_rsrc(a.nw, norm ? (uint32_t)(cols * 4) : 0u);
     // XS_LDS without a norm: the activations of the first kXPre conversion
@@ -943,13 +934,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) xoff[i] = xo + 16u * i;
         }
-        if (x_lds) {
-#pragma unroll
-            for (int k = 0; k < kXLdsLoads; ++k) {
-                const int i = t + k * nthr;
-                xv[k] = bload16(rx, i < n4 ? (uint32_t)i * 16u : kOutOfRange);
-            }
-        } else if (z_lds) {
+        if (z_lds) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int i = t + k * nthr;
@@ -1019,7 +1004,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             const uint4 z = norm4(hv, dv, wv, sv);
             add_sq(sv);
             if (o4) o4[i] = sv;
-            if (z_lds) *reinterpret_cast<uint4 *>(zl + 4 * i) = z;
+            if (z_lds) reinterpret_cast<uint4 *>(zl)[xslot(i)] = z;
         };
         int i0 = t;
         if (z_lds) {   // the first two steps were loaded with x
@@ -1043,21 +1028,11 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     bool wave_f32 = false;
     float s6[4] = {0.f, 0.f, 0.f, 0.f};   // Q6_K: sums of the four quarters
     if (XS == XS_THREAD || XS == XS_F32) {
-        if (x_lds) {
-            uint4 *const xl4 = reinterpret_cast<uint4 *>(xlds);
-#pragma unroll
-            for (int k = 0; k < kXLdsLoads; ++k) {
-                const int i = t + k * nthr;
-                if (i < n4) xl4[i] = xv[k];
-            }
-            for (int i = t + kXLdsLoads * nthr; i < n4; i += nthr)
-                xl4[i] = bload16(rx, (uint32_t)i * 16u);
-            __syncthreads();
-        }
-        if (z_lds || x_lds) {
+        if (z_lds) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                xv[i] = uact ? *reinterpret_cast<const uint4 *>(xlds + xoff[i]) : make_uint4(0, 0, 0, 0);
+                xv[i] = uact ? reinterpret_cast<const uint4 *>(xlds)[17 * u + i]
+                             : make_uint4(0, 0, 0, 0);
         } else if (norm) {
             float4 sv;
 #pragma unroll
@@ -1601,14 +1576,6 @@ int device_cus()
 // workgroup (the gate/up wave groups, the wide lm_head shape).
 constexpr int kSplitThreads = 640;
 
-// The wide shape of a launch: twice the rows per sweep, up to ten waves in
-// one workgroup, where that fits.
-Shape widen(const Shape &sh, bool on)
-{
-    if (on && 2 * sh.threads <= kSplitThreads && sh.rps <= 32) return {2 * sh.rps, 2 * sh.threads};
-    return sh;
-}
-
 // Launch geometry in the arguments: nwg workgroups of nthr threads over
 // `sweeps` sweeps, sq per workgroup and one more for the first srem.
 bool set_launch(RowsArgs &a, int64_t sweeps, int64_t nwg, int nthr)
@@ -1640,13 +1607,11 @@ hipError_t launch_rows(const RowsArgs &a0, int rps, int threads, int64_t nwg, hi
     const dim3 grid((unsigned)nwg, (unsigned)nvec), block((unsigned)threads);
     const int64_t cols = (int64_t)a.nb * kQK;
     const size_t lds = XS == XS_LDS ? (size_t)planes_bytes(cols)
-                       : (a.nw && XS == XS_F32 && cols <= kNormLdsCols) ? (size_t)(cols * 4)
-                       : (Q4K_F32_X_LDS && !a.nw && XS == XS_F32 && cols <= kXLdsCols)
-                           ? (size_t)(cols * 4)
-                                                                         : 0;
-    if constexpr ((EPI == EPI_LOGITS && XS == XS_LDS) ||
-                  (EPI == EPI_STORE && NMAT == 1 && FMT == FMT_Q4K)) {
-        // the wide shape: up to ten waves in one workgroup
+                       : (a.nw && XS == XS_F32 && cols <= kNormLdsCols)
+                           ? (size_t)(cols * 4 * kXPadNum / kXPadDen)
+                           : 0;
+    if constexpr (EPI == EPI_LOGITS && XS == XS_LDS) {
+        // the wide lm_head shape: up to ten waves in one workgroup
         if (threads > 512 && threads <= kSplitThreads && rps > 1) {
             switch (rps) {
 #define Q4K_RPS_CASE(R)                                                                            \
@@ -1796,7 +1761,7 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     a.o2 = o2;
     a.split0 = split0;
     a.split1 = split1;
-    const Shape sh = widen(pick_shape(cols), Q4K_STORE_WIDE);
+    const Shape sh = pick_shape(cols);
     const int64_t nwg = grid_for(rows, cols, sh, Q4K_STORE_WGS_PER_CU);
 #if Q4K_STORE_F32_SWEEPS > 0
     // few sweeps per workgroup: f32 activations, no shared conversion step.
@@ -1854,7 +1819,7 @@ hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, c
     b.o0 = y;
     b.x_stride = inter;
     b.o_stride = hidden;
-    const Shape sd = widen(pick_shape(inter), Q4K_DOWN_WIDE);
+    const Shape sd = pick_shape(inter);
     return launch_rows<1, EPI_STORE, XS_F32, Q4K_DOWN_D>(
         b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s, nvec);
 }
