@@ -998,7 +998,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         ss_part = fmaf(v.z, v.z, ss_part);
         ss_part = fmaf(v.w, v.w, ss_part);
     };
-    if (norm && XS != XS_LDS) {
+    if constexpr (XS != XS_LDS) if (norm) {
         auto pass_step = [&](int i, uint4 hv, uint4 dv, uint4 wv) {
             float4 sv;
             const uint4 z = norm4(hv, dv, wv, sv);
