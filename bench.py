@@ -12,9 +12,13 @@ events, and eager launches of the same step are timed beside it.
 
 Beside the step: the full Q4_K sequence of a layer (QKV, the attention output
 projection 2560 x 2048, FFN) over the 34 layers; the Q6_K matvec at the
-down-projection shape (34 matrices in rotation); and the 64-token prefill FFN
-on the same 34 layers' weights (the matrix-core path), timed per call and
-reported with its MFMA utilisation.
+down-projection shape (34 matrices in rotation); the 64-token prefill FFN on
+the same 34 layers' weights (the matrix-core path), timed per call and
+reported with its MFMA utilisation; every configuration alone (per_config),
+against 8 TB/s and against the read ceiling (the library's own streaming read
+of the same bytes, and an empty launch); the parity of each configuration's
+first repetition against the oracle; and the oracle itself timed on the host
+(cpu_baseline, with per-configuration times).
 
 Prints ONE JSON line (see the fields at the end of main()).
 """
@@ -217,7 +221,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--kernel-only", default="", help="launch only this part (profiling): "
                     "gate_up | down | qkv | lmhead | prefill | q6k | copy (a plain 1 GiB device "
-                    "copy that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+                    "copy that calibrates the FETCH_SIZE / WRITE_SIZE counters) | read_down (the "
+                    "library's streaming-read probe over the down weights, the memory-side "
+                    "reference of the down projection)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill FFN leg")
     ap.add_argument("--no-q6k", action="store_true", help="skip the Q6_K matvec leg")
     ap.add_argument("--no-shard", action="store_true",
@@ -250,7 +256,7 @@ def main() -> int:
     # ---------------------------------------------------------------- inputs
     t0 = time.perf_counter()
     qkv_host, ffn_host, qkv_dev, ffn_dev, o_dev = [], [], [], [], []
-    need_layers = args.kernel_only in ("", "gate_up", "down", "qkv", "prefill")
+    need_layers = args.kernel_only in ("", "gate_up", "down", "qkv", "prefill", "read_down")
     for l in range(LAYERS if need_layers else 0):
         c = inputs.qkv(copy=l)
         L = inputs.ffn_layer(l)
@@ -366,7 +372,10 @@ def main() -> int:
             "lmhead": run_lmhead,
             "prefill": run_prefill,
             "q6k": run_q6k,
+            "read_down": lambda: [q4k.q4k_probe_read(L["Wd"], L["Wd"].numel(), 256, 512, 8, False,
+                                                     probe_sink) for L in ffn_dev],
         }
+        probe_sink = torch.zeros(1, dtype=torch.int32, device=dev)
         fn = parts[args.kernel_only]
         for i in range(args.warmup + args.steps):
             fn()
