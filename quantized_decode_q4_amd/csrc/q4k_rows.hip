@@ -801,6 +801,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     __shared__ float lg[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
     __shared__ uint64_t wave_lists[EPI == EPI_LOGITS ? NW : 1][EPI == EPI_LOGITS ? kTopkMax : 1];
     __shared__ float sum_scratch[EPI == EPI_LOGITS ? NW : 1];
+    __shared__ uint64_t max_scratch[EPI == EPI_LOGITS ? NW : 1];
+    __shared__ float base_scratch[EPI == EPI_LOGITS ? NW : 1];
     __shared__ float norm_scratch[NW];
     extern __shared__ uint4 xlds_v[];   // XS_LDS: planes of x (planes_bytes(cols))
     uint8_t *const xlds = reinterpret_cast<uint8_t *>(xlds_v);
@@ -1336,43 +1338,84 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     }
 
     if (EPI == EPI_LOGITS) {
-        // Per-workgroup top-k of its rows, written in rank order. Each wave
-        // takes the top-k of a contiguous slice of the rows, held as orderable
-        // keys in registers: k rounds of a lane maximum and a wave maximum, the
-        // lane holding the winner clearing it (keys are unique: they embed the
-        // row). No barrier or LDS access inside the rounds. Wave 0 then merges
-        // the waves' lists the same way.
+        // Per-workgroup top-k of its rows, written in rank order, and (with
+        // stats) the workgroup's softmax partial, computed side by side: four
+        // waves (one per SIMD) each take the top-k of a quarter of the rows,
+        // held as orderable keys in registers (k rounds of a lane maximum and
+        // a wave maximum, the lane holding the winner clearing it; keys are
+        // unique: they embed the row), while each other wave forms the partial
+        // of its share of the rows. Wave 0 then merges the four lists the same
+        // way, and the partials are combined beside it.
         __syncthreads();
         // local row j = i * RPS + rr is global row gsweep(i) * RPS + rr; rows
         // past the end (a partial last sweep) are skipped
         const int n = (int)(n_loc * RPS);
         auto grow = [&](int j) -> int64_t { return gsweep(j / RPS) * RPS + j % RPS; };
         uint64_t *out = a.cand + (int64_t)blockIdx.x * a.k;
-        // slices of at most kLmheadRowsPerWgMax / 4 rows: every launch has >= 4 waves
-        constexpr int kKeysPerLane = kLmheadRowsPerWgMax / (4 * 64);
-        const int per_wave = (n + nwaves - 1) / nwaves;
-        const int cpl = (per_wave + 63) / 64;
-        uint64_t key[kKeysPerLane];
-#pragma unroll
-        for (int c = 0; c < kKeysPerLane; ++c) {
-            const int o = c * 64 + lane;
-            const int j = wave * per_wave + o;
-            uint64_t kk = 0;
-            if (c < cpl && o < per_wave && j < n) {
+        constexpr int kTkWaves = 4;   // every launch has at least four waves
+        // quarters of at most kLmheadRowsPerWgMax / 4 rows
+        constexpr int kKeysPerLane = kLmheadRowsPerWgMax / (kTkWaves * 64);
+        const bool stats = a.stats != nullptr;
+        const int swaves = nwaves - kTkWaves;   // waves that sum the exponentials
+        // Softmax partial of the workgroup: m = its largest logit (its first
+        // winner: the largest key, NaN lowest), s = sum of exp(l - m). When m
+        // is -inf (every row -inf or NaN) the exponent is taken against 0
+        // instead, so that -inf rows add 0 and NaN rows poison the sum. A
+        // share of the rows gives (m_w, s_w) the same way (base b_w), and the
+        // shares combine as s = sum over s_w != 0 of s_w exp(b_w - b): b_w <= b,
+        // so no term overflows, and a NaN s_w still poisons the sum.
+        auto share_partial = [&](int j0, int step, uint64_t &mk, float &bw, float &sw) {
+            mk = 0;
+            for (int j = j0; j < n; j += step) {
                 const int64_t gr = grow(j);
-                if (gr < a.rows) kk = topk_key(lg[j], (uint32_t)gr);
+                if (gr < a.rows) {
+                    const uint64_t kk = topk_key(lg[j], (uint32_t)gr);
+                    mk = kk > mk ? kk : mk;
+                }
             }
-            key[c] = kk;
+            mk = wave_max_u64(mk);
+            const float mw = topk_key_value(mk);
+            bw = mw == -INFINITY ? 0.f : mw;
+            sw = 0.f;
+            for (int j = j0; j < n; j += step)
+                if (grow(j) < a.rows) sw += expf(lg[j] - bw);
+            sw = wave_sum_mod<1>(sw);
+        };
+        if (wave < kTkWaves) {
+            const int per_wave = (n + kTkWaves - 1) / kTkWaves;
+            const int cpl = (per_wave + 63) / 64;
+            uint64_t key[kKeysPerLane];
+#pragma unroll
+            for (int c = 0; c < kKeysPerLane; ++c) {
+                const int o = c * 64 + lane;
+                const int j = wave * per_wave + o;
+                uint64_t kk = 0;
+                if (c < cpl && o < per_wave && j < n) {
+                    const int64_t gr = grow(j);
+                    if (gr < a.rows) kk = topk_key(lg[j], (uint32_t)gr);
+                }
+                key[c] = kk;
+            }
+            wave_topk(key, cpl, a.k, wave_lists[wave], lane);
         }
-        wave_topk(key, cpl, a.k, wave_lists[wave], lane);
+        // the waves beyond the four take the partial; four-wave launches take it
+        // after their lists (every wave a quarter of the rows)
+        if (stats && (wave >= kTkWaves || swaves == 0)) {
+            const int sw_idx = swaves > 0 ? wave - kTkWaves : wave;
+            const int sw_n = swaves > 0 ? swaves : nwaves;
+            uint64_t mk;
+            float bw, sw;
+            share_partial(lane + 64 * sw_idx, 64 * sw_n, mk, bw, sw);
+            if (lane == 0) {
+                max_scratch[sw_idx] = mk;
+                base_scratch[sw_idx] = bw;
+                sum_scratch[sw_idx] = sw;
+            }
+        }
         __syncthreads();
-        // the workgroup's largest logit: the largest of the waves' first winners
-        uint64_t top = 0;
-        for (int w = 0; w < nwaves; ++w) top = wave_lists[w][0] > top ? wave_lists[w][0] : top;
-        const float wg_max = topk_key_value(top);
         if (wave == 0) {
-            constexpr int kMergePerLane = NW * kTopkMax / 64;
-            const int total = nwaves * a.k;
+            constexpr int kMergePerLane = kTkWaves * kTopkMax / 64;
+            const int total = kTkWaves * a.k;
             const int mpl = (total + 63) / 64;
             uint64_t m[kMergePerLane];
 #pragma unroll
@@ -1381,18 +1424,16 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 m[c] = (c < mpl && i < total) ? wave_lists[i / a.k][i % a.k] : 0ull;
             }
             wave_topk(m, mpl, a.k, out, lane);
-        }
-        if (a.stats) {
-            // softmax partial of this workgroup: m = its largest logit (the
-            // first winner), s = sum of exp(l - m). When m is -inf (every row
-            // -inf or NaN) the exponent is taken against 0 instead, so that -inf
-            // rows add 0 and NaN rows poison the sum.
+        } else if (stats && t == 64) {   // beside wave 0's merge
+            const int nsum = swaves > 0 ? swaves : nwaves;
+            uint64_t mk = 0;
+            for (int w = 0; w < nsum; ++w) mk = max_scratch[w] > mk ? max_scratch[w] : mk;
+            const float wg_max = topk_key_value(mk);
             const float base = wg_max == -INFINITY ? 0.f : wg_max;
             float sum = 0.f;
-            for (int j = t; j < n; j += nthr)
-                if (grow(j) < a.rows) sum += expf(lg[j] - base);
-            sum = block_sum_f32(sum, sum_scratch, nwaves);
-            if (t == 0) a.stats[blockIdx.x] = make_float2(wg_max, sum);
+            for (int w = 0; w < nsum; ++w)
+                if (sum_scratch[w] != 0.f) sum += sum_scratch[w] * expf(base_scratch[w] - base);
+            a.stats[blockIdx.x] = make_float2(wg_max, sum);
         }
     }
 }
