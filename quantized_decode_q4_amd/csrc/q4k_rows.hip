@@ -173,6 +173,7 @@ struct RowsArgs {
     int32_t srem;
     int32_t nwg;             // gridDim.x
     int32_t nthr;            // blockDim.x
+    int32_t xpass;           // (cols / 8 + nthr - 1) / nthr: passes of a workgroup-wide conversion
     int32_t ilv;             // 1: workgroup w takes sweeps w, w+G, w+2G, ... (else a contiguous range)
     // Several activation vectors in one launch (grid row y = vector y): x
     // and o0 advance by these many floats per vector (o1, o2 unused then).
@@ -189,7 +190,7 @@ __device__ __forceinline__ void args_to_sgprs(const RowsArgs &a)
     asm volatile("" ::"s"(a.W0), "s"(a.W1), "s"(a.x), "s"(a.o0), "s"(a.o1), "s"(a.o2),
                  "s"(a.cand), "s"(a.stats), "s"(a.delta), "s"(a.nw), "s"(a.h_out), "s"(a.eps),
                  "s"(a.rows), "s"(a.split0), "s"(a.split1), "s"(a.nb), "s"(a.U), "s"(a.act),
-                 "s"(a.k), "s"(a.sq), "s"(a.srem), "s"(a.nwg), "s"(a.nthr), "s"(a.ilv),
+                 "s"(a.k), "s"(a.sq), "s"(a.srem), "s"(a.nwg), "s"(a.nthr), "s"(a.xpass), "s"(a.ilv),
                  "s"(a.x_stride), "s"(a.o_stride));
 }
 
@@ -814,7 +815,8 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // wave group of the thread (uniform across a wave: the group size is a
     // multiple of 64), its thread and wave index inside the group
     const int gsz = nthr / NG;
-    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(t / gsz);
+    static_assert(NG == 1 || NG == 2, "one or two wave groups");
+    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(t >= gsz ? 1 : 0);
     const int tl = t - grp * gsz;
     const int gwave = tl >> 6;
     // sweeps per reduction batch: every row of a batch needs a thread
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // activation planes in LDS: one copy per wave group when each wave converts
     // its own (no barrier between the groups), else one shared copy
     uint8_t *const xp = xlds + (wave_local ? (int64_t)grp * planes_bytes(cols) : 0);
-    const int gpasses = wave_local ? (gpw + 63) / 64 : (ngroups + nthr - 1) / nthr;
+    const int gpasses = wave_local ? (gpw + 63) / 64 : a.xpass;
     // group of pass i of this thread, or ngroups for none
     auto group_of = [&](int i) -> int {
         if (wave_local) {
@@ -1626,6 +1628,7 @@ bool set_launch(RowsArgs &a, int64_t sweeps, int64_t nwg, int nthr)
     a.srem = (int32_t)(sweeps % nwg);
     a.nwg = (int32_t)nwg;
     a.nthr = nthr;
+    a.xpass = (int32_t)(((int64_t)a.nb * (kQK / 8) + nthr - 1) / nthr);
     return true;
 }
 
