@@ -731,6 +731,35 @@ __device__ __forceinline__ void wave_topk(uint64_t (&key)[MAXC], int nc, int k, 
         wave_topk_n<MAXC>(key, k, dst, lane);
 }
 
+// Top-k of NL lists of k <= kRankMax keys each (list w at lists[w * STRIDE],
+// in LDS) in one pass instead of k dependent rounds: every key is read by
+// every lane (all reads issued before the first compare), lane i takes key
+// (i / kRankMax, i % kRankMax) and counts the keys above it. Nonzero keys are
+// unique (they embed the row), so they get the distinct ranks 0 .. nz - 1;
+// the key of rank r < k goes to dst[r] and dst[nz .. k) gets 0 (no
+// candidate), as wave_topk writes. Every slot has exactly one writer.
+constexpr int kRankMax = 8;
+template <int NL, int STRIDE>
+__device__ __forceinline__ void wave_rank_merge(const uint64_t *lists, int k, uint64_t *dst,
+                                                int lane)
+{
+    static_assert(NL * kRankMax <= 64, "one key per lane");
+    uint64_t all[NL * kRankMax];
+#pragma unroll
+    for (int w = 0; w < NL; ++w)
+#pragma unroll
+        for (int r = 0; r < kRankMax; ++r) all[w * kRankMax + r] = r < k ? lists[w * STRIDE + r] : 0ull;
+    const int lw = lane / kRankMax, lr = lane % kRankMax;
+    const uint64_t mine = (lw < NL && lr < k) ? lists[lw * STRIDE + lr] : 0ull;
+    int above[4] = {0, 0, 0, 0};   // four partial counts: shorter dependence chains
+#pragma unroll
+    for (int j = 0; j < NL * kRankMax; ++j) above[j & 3] += all[j] > mine ? 1 : 0;
+    const int rank = (above[0] + above[1]) + (above[2] + above[3]);
+    const int nz = __popcll(__ballot(mine != 0ull));
+    if (mine != 0ull && rank < k) dst[rank] = mine;
+    if (lane >= nz && lane < k) dst[lane] = 0ull;
+}
+
 // Workgroup-wide maximum of a key with one barrier: wave maxima go to
 // scratch[wave], which the caller alternates between two buffers from one
 // call to the next (a buffer is rewritten only after the next call's
@@ -1416,16 +1445,20 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
         }
         __syncthreads();
         if (wave == 0) {
-            constexpr int kMergePerLane = kTkWaves * kTopkMax / 64;
-            const int total = kTkWaves * a.k;
-            const int mpl = (total + 63) / 64;
-            uint64_t m[kMergePerLane];
+            if (a.k <= kRankMax) {
+                wave_rank_merge<kTkWaves, kTopkMax>(&wave_lists[0][0], a.k, out, lane);
+            } else {
+                constexpr int kMergePerLane = kTkWaves * kTopkMax / 64;
+                const int total = kTkWaves * a.k;
+                const int mpl = (total + 63) / 64;
+                uint64_t m[kMergePerLane];
 #pragma unroll
-            for (int c = 0; c < kMergePerLane; ++c) {
-                const int i = c * 64 + lane;
-                m[c] = (c < mpl && i < total) ? wave_lists[i / a.k][i % a.k] : 0ull;
+                for (int c = 0; c < kMergePerLane; ++c) {
+                    const int i = c * 64 + lane;
+                    m[c] = (c < mpl && i < total) ? wave_lists[i / a.k][i % a.k] : 0ull;
+                }
+                wave_topk(m, mpl, a.k, out, lane);
             }
-            wave_topk(m, mpl, a.k, out, lane);
         } else if (stats && t == 64) {   // beside wave 0's merge
             const int nsum = swaves > 0 ? swaves : nwaves;
             uint64_t mk = 0;
@@ -1492,16 +1525,20 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_
         wave_topk(key, cpl, k, wave_wins[wave], lane);
         __syncthreads();
         if (wave == 0) {
-            constexpr int kPer = kMergeWaves * kTopkMax / 64;
-            const int tot2 = kMergeWaves * k;
-            const int mpl = (tot2 + 63) / 64;
-            uint64_t m[kPer];
+            if (k <= kRankMax) {
+                wave_rank_merge<kMergeWaves, kTopkMax>(&wave_wins[0][0], k, wins, lane);
+            } else {
+                constexpr int kPer = kMergeWaves * kTopkMax / 64;
+                const int tot2 = kMergeWaves * k;
+                const int mpl = (tot2 + 63) / 64;
+                uint64_t m[kPer];
 #pragma unroll
-            for (int c = 0; c < kPer; ++c) {
-                const int i = c * 64 + lane;
-                m[c] = (c < mpl && i < tot2) ? wave_wins[i / k][i % k] : 0ull;
+                for (int c = 0; c < kPer; ++c) {
+                    const int i = c * 64 + lane;
+                    m[c] = (c < mpl && i < tot2) ? wave_wins[i / k][i % k] : 0ull;
+                }
+                wave_topk(m, mpl, k, wins, lane);
             }
-            wave_topk(m, mpl, k, wins, lane);
         }
     } else {
         const bool in_lds = total <= kMergeLdsKeys;
