@@ -778,14 +778,20 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *scratch)
 
 // Workgroup-wide sum over nwaves waves with one barrier (fixed order:
 // deterministic).
+template <int MAXW>
 __device__ __forceinline__ float block_sum_f32(float v, float *scratch, int nwaves)
 {
     v = wave_sum_mod<1>(v);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (lane == 0) scratch[wave] = v;
     __syncthreads();
-    float r = scratch[0];
-    for (int w = 1; w < nwaves; ++w) r += scratch[w];
+    float p[MAXW];   // every slot read at once, then added in wave order
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) p[w] = scratch[w];
+    float r = p[0];
+#pragma unroll
+    for (int w = 1; w < MAXW; ++w)
+        if (w < nwaves) r += p[w];
     return r;
 }
 
@@ -1049,7 +1055,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             const uint32_t off = (uint32_t)i * 16u;
             pass_step(i, bload16(rx, off), bload16(rdel, off), bload16(rnw, off));
         }
-        const float ss = block_sum_f32(ss_part, norm_scratch, nwaves);   // also publishes zl
+        const float ss = block_sum_f32<NW>(ss_part, norm_scratch, nwaves);   // also publishes zl
         inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
     }
 
@@ -1213,7 +1219,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
             convert(e, h0, h1, d0, d1, w0, w1);
         }
         if (norm) {
-            const float ss = block_sum_f32(ss_part, norm_scratch, nwaves);   // also publishes the planes
+            const float ss = block_sum_f32<NW>(ss_part, norm_scratch, nwaves);   // also publishes the planes
             inv_rms = 1.f / sqrtf(ss / (float)cols + a.eps);
         } else if (wave_local) {
             // the wave reads back only what it wrote: keep the compiler from
@@ -1308,18 +1314,39 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 const int64_t li = sj - kb + 1 + k;         // local sweep of this row
                 const int64_t row = gsweep(li) * RPS + rr;
                 if (row < a.rows) {
+                    // Wave partials added in wave order. Every slot a launch
+                    // of this shape can hold is read first (all reads in
+                    // flight together), and only the waves present are added.
                     float v0 = 0.f, v1 = 0.f;
                     if (NG == 1) {
-                        for (int w = 0; w < nwaves; ++w) {
-                            v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
-                            if (NMAT == 2) v1 += red[bank][w][(k * NMAT + 1) * RPS + rr];
+                        float p0[NW], p1[NW];
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) {
+                            p0[w] = red[bank][w][(k * NMAT + 0) * RPS + rr];
+                            p1[w] = NMAT == 2 ? red[bank][w][(k * NMAT + 1) * RPS + rr] : 0.f;
+                        }
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) {
+                            if (w < nwaves) {
+                                v0 += p0[w];
+                                if (NMAT == 2) v1 += p1[w];
+                            }
                         }
                     } else {
                         // gate partials from the first group's waves, up from the second's
                         const int gw = nwaves / 2;
-                        for (int w = 0; w < gw; ++w) {
-                            v0 += red[bank][w][(k * NMAT + 0) * RPS + rr];
-                            v1 += red[bank][gw + w][(k * NMAT + 1) * RPS + rr];
+                        float p0[NW / 2], p1[NW / 2];
+#pragma unroll
+                        for (int w = 0; w < NW / 2; ++w) {
+                            p0[w] = red[bank][w][(k * NMAT + 0) * RPS + rr];
+                            p1[w] = red[bank][gw + w][(k * NMAT + 1) * RPS + rr];
+                        }
+#pragma unroll
+                        for (int w = 0; w < NW / 2; ++w) {
+                            if (w < gw) {
+                                v0 += p0[w];
+                                v1 += p1[w];
+                            }
                         }
                     }
                     if (norm) {
@@ -1460,14 +1487,26 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
                 wave_topk(m, mpl, a.k, out, lane);
             }
         } else if (stats && t == 64) {   // beside wave 0's merge
+            // all of the shares' partials read at once, then combined in order
             const int nsum = swaves > 0 ? swaves : nwaves;
+            uint64_t pm[NW];
+            float pb[NW], ps[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                pm[w] = max_scratch[w];
+                pb[w] = base_scratch[w];
+                ps[w] = sum_scratch[w];
+            }
             uint64_t mk = 0;
-            for (int w = 0; w < nsum; ++w) mk = max_scratch[w] > mk ? max_scratch[w] : mk;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                if (w < nsum) mk = pm[w] > mk ? pm[w] : mk;
             const float wg_max = topk_key_value(mk);
             const float base = wg_max == -INFINITY ? 0.f : wg_max;
             float sum = 0.f;
-            for (int w = 0; w < nsum; ++w)
-                if (sum_scratch[w] != 0.f) sum += sum_scratch[w] * expf(base_scratch[w] - base);
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                if (w < nsum && ps[w] != 0.f) sum += ps[w] * expf(pb[w] - base);
             a.stats[blockIdx.x] = make_float2(wg_max, sum);
         }
     }
@@ -1595,7 +1634,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_
 #pragma unroll
         for (int i = 0; i < kMergeListsPerThread; ++i)
             if (st[i].y != 0.f) sum += st[i].y * expf(st[i].x - base);  // NaN partials propagate
-        S = block_sum_f32(sum, sum_scratch, kMergeWaves);
+        S = block_sum_f32<kMergeWaves>(sum, sum_scratch, kMergeWaves);
     }
     if (t < k) {
         const uint64_t win = wins[t];
