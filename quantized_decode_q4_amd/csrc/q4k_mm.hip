@@ -641,19 +641,29 @@ __global__ __launch_bounds__(256) void x_to_frag_kernel(const float *X, uint8_t 
     *reinterpret_cast<bf16x8 *>(Xf + frag_offset(token, k0, cols >> 8)) = v;
 }
 
-// K splits: Y[t][i] = sum_s P[s][t][i], s in order.
+constexpr int kReduceBatch = 8;   // split loads in flight per thread
+
+// K splits: Y[t][i] = sum_s P[s][t][i], s in order; a batch of splits' loads
+// is issued before its sums.
 __global__ __launch_bounds__(256) void reduce_y_kernel(const float *P, float *Y, int64_t n, int S)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float acc = P[i];
-    for (int s = 1; s < S; ++s) acc += P[(int64_t)s * n + i];
+    for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
+        float v[kReduceBatch];
+#pragma unroll
+        for (int k = 0; k < kReduceBatch; ++k)
+            if (s0 + k < S) v[k] = P[(int64_t)(s0 + k) * n + i];
+#pragma unroll
+        for (int k = 0; k < kReduceBatch; ++k)
+            if (s0 + k < S) acc += v[k];
+    }
     Y[i] = acc;
 }
 
 // The same, four consecutive outputs per thread (n % 4 == 0, Y 16-byte
 // aligned): one 16-byte load per split, all issued before the sums.
-constexpr int kReduceBatch = 8;
 __global__ __launch_bounds__(256) void reduce_y4_kernel(const float4 *P, float4 *Y, int64_t n4, int S)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -690,9 +700,20 @@ __global__ __launch_bounds__(256) void reduce_gated_kernel(const float *P, uint8
         const int64_t stride = seq * 2 * inter;
         const float *pg = P + token * 2 * inter + i;
         float g = pg[0], u = pg[inter];
-        for (int s = 1; s < S; ++s) {
-            g += pg[s * stride];
-            u += pg[s * stride + inter];
+        for (int s0 = 1; s0 < S; s0 += kReduceBatch) {   // a batch of loads, then its sums
+            float vg[kReduceBatch], vu[kReduceBatch];
+#pragma unroll
+            for (int k = 0; k < kReduceBatch; ++k)
+                if (s0 + k < S) {
+                    vg[k] = pg[(s0 + k) * stride];
+                    vu[k] = pg[(s0 + k) * stride + inter];
+                }
+#pragma unroll
+            for (int k = 0; k < kReduceBatch; ++k)
+                if (s0 + k < S) {
+                    g += vg[k];
+                    u += vu[k];
+                }
         }
         h = act_apply(g, act) * u;
     }
