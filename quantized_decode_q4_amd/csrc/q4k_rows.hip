@@ -68,7 +68,10 @@
 #define Q4K_ROWS_FB 8               // sweeps per cross-wave reduction batch
 #endif
 #ifndef Q4K_STORE_D
-#define Q4K_STORE_D 1               // sweeps in flight, matvec / QKV
+#define Q4K_STORE_D 1               // sweeps in flight, block-floating-point matvec
+#endif
+#ifndef Q4K_F32_DEEP_SWEEPS
+#define Q4K_F32_DEEP_SWEEPS 4       // f32 launches: two sweeps in flight from this many per workgroup
 #endif
 #ifndef Q4K_STORE_WGS_PER_CU
 #define Q4K_STORE_WGS_PER_CU 1
@@ -84,9 +87,6 @@
 #endif
 #ifndef Q4K_GATE_UP_SPLIT
 #define Q4K_GATE_UP_SPLIT 1         // gate and up rows in two wave groups (where both fit)
-#endif
-#ifndef Q4K_DOWN_D
-#define Q4K_DOWN_D 1
 #endif
 #ifndef Q4K_DOWN_WGS_PER_CU
 #define Q4K_DOWN_WGS_PER_CU 1
@@ -1865,6 +1865,20 @@ void set_norm(RowsArgs &a, const NormIn *norm)
     a.h_out = norm->h_out;
 }
 
+// The f32-activation matvec launches (QKV, the short matvecs, the FFN's down
+// projection): two sweeps in flight once a workgroup runs at least
+// Q4K_F32_DEEP_SWEEPS of them, else one. At 2560x10240 (five per workgroup)
+// two gave 6.86-6.93 us against 7.00-7.11; QKV (two per workgroup) was 0.1 us
+// slower with two.
+hipError_t launch_f32_store(const RowsArgs &a, const Shape &sh, int64_t nwg, hipStream_t s,
+                            int64_t nvec)
+{
+    const int64_t sweeps = (a.rows + sh.rps - 1) / sh.rps;
+    if (sweeps >= (int64_t)Q4K_F32_DEEP_SWEEPS * nwg)
+        return launch_rows<1, EPI_STORE, XS_F32, 2>(a, sh.rps, sh.threads, nwg, s, nvec);
+    return launch_rows<1, EPI_STORE, XS_F32, 1>(a, sh.rps, sh.threads, nwg, s, nvec);
+}
+
 hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float *o1, float *o2,
                              int64_t rows, int64_t cols, int64_t split0, int64_t split1,
                              hipStream_t s, const NormIn *norm, const Batch &bt)
@@ -1891,9 +1905,7 @@ hipError_t launch_rows_store(const uint8_t *W, const float *x, float *o0, float 
     // 16384x2560 (RPS 8, 8 sweeps) block floating point 8.1 us against 8.8 us.
     const int64_t sweeps = (rows + sh.rps - 1) / sh.rps;
     const int64_t f32_sweeps = (int64_t)Q4K_STORE_F32_SWEEPS * (sh.rps < 8 ? 8 / sh.rps : 1);
-    if (sweeps <= f32_sweeps * nwg)
-        return launch_rows<1, EPI_STORE, XS_F32, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s,
-                                                              bt.nvec);
+    if (sweeps <= f32_sweeps * nwg) return launch_f32_store(a, sh, nwg, s, bt.nvec);
 #endif
     return launch_rows_bfp<1, EPI_STORE, Q4K_STORE_D>(a, sh.rps, sh.threads, nwg, s, bt.nvec);
 }
@@ -1940,8 +1952,7 @@ hipError_t launch_ffn(const uint8_t *Wg, const uint8_t *Wu, const uint8_t *Wd, c
     b.x_stride = inter;
     b.o_stride = hidden;
     const Shape sd = pick_shape(inter);
-    return launch_rows<1, EPI_STORE, XS_F32, Q4K_DOWN_D>(
-        b, sd.rps, sd.threads, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s, nvec);
+    return launch_f32_store(b, sd, grid_for(hidden, inter, sd, Q4K_DOWN_WGS_PER_CU), s, nvec);
 }
 
 hipError_t launch_q6k_matvec(const uint8_t *W, const float *x, float *y, int64_t rows,
