@@ -326,10 +326,19 @@ Q4K_EXPORT int64_t q4k_lmhead_rows_max(int64_t cols)
     return q4k::lmhead_rows_max(cols);
 }
 
+// The vocabulary limit, the same test for the workspace size and the calls:
+// at most lmhead_rows_max(cols) rows, which keeps the candidate lists within
+// what the merge kernel takes.
+static bool lmhead_rows_fit(int64_t rows, int64_t cols)
+{
+    return rows <= q4k::lmhead_rows_max(cols) &&
+           q4k::lmhead_max_wgs(rows, cols) <= q4k::kMergeListsMax;
+}
+
 Q4K_EXPORT size_t q4k_lmhead_workspace_bytes(int64_t rows, int64_t cols, int k)
 {
     if (!rows_ok(rows) || !cols_ok(cols) || rows == 0 || k < 1 || k > Q4K_TOPK_MAX) return 0;
-    if (rows > q4k::lmhead_rows_max(cols)) return 0;
+    if (!lmhead_rows_fit(rows, cols)) return 0;
     return lmhead_cand_bytes(rows, cols, k) +
            round_up((size_t)q4k::lmhead_max_wgs(rows, cols) * 8, 256);
 }
@@ -342,9 +351,7 @@ static int lmhead_call(const void *W, const float *x, float *logits, int64_t row
 {
     if (!rows_ok(rows) || !cols_ok(cols)) return Q4K_ERR_SHAPE;
     if (k < 1 || k > Q4K_TOPK_MAX || k > rows) return Q4K_ERR_K;
-    if (rows > q4k::lmhead_rows_max(cols) ||
-        q4k::lmhead_max_wgs(rows, cols) > q4k::kMergeListsMax)
-        return Q4K_ERR_SHAPE;
+    if (!lmhead_rows_fit(rows, cols)) return Q4K_ERR_SHAPE;
     if (!W || !x || !logits || !top_idx || !top_val) return Q4K_ERR_NULL;
     if (probs && (!top_prob || !lse)) return Q4K_ERR_NULL;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(logits, 4) || !aligned(top_idx, 4) ||

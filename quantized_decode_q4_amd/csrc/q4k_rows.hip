@@ -1989,8 +1989,11 @@ LmShape lmhead_shape(int64_t cols)
 // rows, and no more than there are sweeps.
 int64_t lmhead_grid(int64_t rows, const Shape &sh, int64_t g)
 {
+    // ceil(S * rps / (kLmheadRowsPerWgMax - rps)) workgroups: then none takes
+    // more than kLmheadRowsPerWgMax / rps sweeps
     const int64_t S = (rows + sh.rps - 1) / sh.rps;
-    const int64_t min_g = (S * sh.rps + kLmheadRowsPerWgMax - 1) / (kLmheadRowsPerWgMax - sh.rps);
+    const int64_t per_wg = kLmheadRowsPerWgMax - sh.rps;
+    const int64_t min_g = (S * sh.rps + per_wg - 1) / per_wg;
     if (g < min_g) g = min_g;
     return S < g ? S : g;
 }

@@ -184,10 +184,17 @@ def test_lmhead_row_limit():
     """The vocabulary limit the header states: rows up to q4k_lmhead_rows_max
     size a workspace, one more is refused by the calls before any launch."""
     L = q4k.lib
+    rup = lambda n: (n + 255) // 256 * 256
     for cols in (256, 512, 2560, 4096, 16384, 65536):
         rmax = L.q4k_lmhead_rows_max(cols)
         assert rmax >= 4_000_000, (cols, rmax)
-        assert L.q4k_lmhead_workspace_bytes(rmax, cols, 5) > 0
+        # the workspace and the calls share one test; at the limit the grid is
+        # exactly the 1024 candidate lists the merge takes (k keys and one
+        # softmax partial each)
+        for rows in (rmax, rmax - 1, rmax - 63, rmax // 2 + 1):
+            assert L.q4k_lmhead_workspace_bytes(rows, cols, 5) > 0, (cols, rows)
+        assert L.q4k_lmhead_workspace_bytes(rmax, cols, 5) == rup(1024 * 5 * 8) + rup(1024 * 8)
+        assert L.q4k_lmhead_workspace_bytes(rmax, cols, 64) == rup(1024 * 64 * 8) + rup(1024 * 8)
         assert L.q4k_lmhead_workspace_bytes(rmax + 1, cols, 5) == 0
         assert L.q4k_lmhead_topk(A, B, C, rmax + 1, cols, 5, D, E, F, 1 << 40, S) == \
             q4k.Q4K_ERR_SHAPE
