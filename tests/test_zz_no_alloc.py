@@ -57,6 +57,24 @@ def test_noalloc_ffn_two_calls_second_smaller(q4k, orc):
         assert err.max() <= 1e-4
 
 
+def test_noalloc_ffn_at_the_scratch_limit(q4k, orc):
+    """inter = Q4K_NOALLOC_INTER_MAX exactly fills the scratch: still equal to
+    q4k_ffn bit for bit, and to the oracle within the f32 bound."""
+    hidden, inter, act = 256, q4k.Q4K_NOALLOC_INTER_MAX, 0
+    print(f"ffn_noalloc hidden={hidden} inter={inter} (the scratch limit)", flush=True)
+    rng = np.random.default_rng(11)
+    Wg = inputs.q4k_random(rng, inter, hidden)
+    Wu = inputs.q4k_random(rng, inter, hidden)
+    Wd = inputs.q4k_random(rng, hidden, inter)
+    x = inputs.normal_f32(rng, hidden)
+    y, y_ref = ffn_both(q4k, dev(Wg), dev(Wu), dev(Wd), dev(x), hidden, inter, act)
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+    r = orc.ffn(Wg, Wu, Wd, x, hidden, inter, act)
+    err = np.abs(y.astype(np.float64) - r["y"]) / r["A"]
+    print(f"  max |err|/A = {err.max():.3e}", flush=True)
+    assert err.max() <= 1e-4
+
+
 def test_noalloc_ffn_refuses_inter_beyond_the_scratch(q4k):
     hidden, inter = 256, q4k.Q4K_NOALLOC_INTER_MAX + 256
     W = torch.zeros(inter * 144, dtype=torch.uint8, device="cuda")
