@@ -51,7 +51,7 @@ def gpu_norm_matvec(q4k, W, h, delta, w, eps, rows, cols, want_h_out=True):
 # (activations converted in LDS), rows wider than the LDS copy (per-thread
 # conversion), ragged and tiny shapes.
 SHAPES = [(1, 256), (100, 512), (4096, 2560), (2560, 2048), (30000, 1024), (10240, 2560),
-          (300, 20480), (777, 768)]
+          (300, 20480), (777, 768), (3, 65536)]
 
 
 @pytest.mark.parametrize("rows,cols", SHAPES)
@@ -113,7 +113,8 @@ def test_rmsnorm_scale_invariance_on_gpu(q4k, orc):
     check(y2, ref, A, "scale 2^40")
 
 
-@pytest.mark.parametrize("hidden,inter,act", [(512, 768, 0), (1024, 3072, 1), (2560, 10240, 0)])
+@pytest.mark.parametrize("hidden,inter,act", [(512, 768, 0), (1024, 3072, 1), (2560, 10240, 0),
+                                              (65536, 512, 1)])
 def test_rmsnorm_ffn(q4k, orc, hidden, inter, act):
     print(f"rmsnorm_ffn hidden={hidden} inter={inter} act={act}", flush=True)
     if hidden == inputs.HIDDEN:
