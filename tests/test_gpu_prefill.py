@@ -91,6 +91,7 @@ MATMUL_SHAPES = [
     (2560, 2560, 128),
     (40, 65536, 64),       # the largest cols: K split 256 ways, one super-block each
     (300, 65536, 70),      # ... 32 ways, with two token groups
+    (1000, 2560, 520),     # nine token groups, the last ragged
 ]
 
 
@@ -200,6 +201,7 @@ FFN_SHAPES = [
     (8192, 512, 64, 1),    # gate/up pair split along K (16 splits)
     (4096, 512, 130, 0),   # ... with three token groups
     (256, 65536, 64, 0),   # down reduces over the largest cols (K split 64 ways)
+    (65536, 256, 64, 1),   # gate/up over the largest cols, down over the most rows
 ]
 
 
