@@ -67,6 +67,9 @@
 #ifndef Q4K_ROWS_FB
 #define Q4K_ROWS_FB 8               // sweeps per cross-wave reduction batch
 #endif
+#ifndef Q4K_LMHEAD_FB
+#define Q4K_LMHEAD_FB 4             // the same for lm_head (64 sweeps per workgroup at 262144 rows)
+#endif
 #ifndef Q4K_STORE_D
 #define Q4K_STORE_D 1               // sweeps in flight, block-floating-point matvec
 #endif
@@ -831,7 +834,7 @@ __global__ __launch_bounds__(MAXT) void rows_kernel(RowsArgs a)
     // matrices one thread streams
     constexpr int LM = NG == 2 ? 1 : NMAT;
     constexpr int NW = MAXT / 64;
-    constexpr int FB = Q4K_ROWS_FB;
+    constexpr int FB = EPI == EPI_LOGITS ? Q4K_LMHEAD_FB : Q4K_ROWS_FB;
     constexpr bool kInt = XS != XS_F32;
     __shared__ float red[2][NW][FB * NMAT * RPS];
     __shared__ float lg[EPI == EPI_LOGITS ? kLmheadRowsPerWgMax : 1];
